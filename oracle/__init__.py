@@ -1,0 +1,140 @@
+"""ctypes front end of the CPU oracle (``pa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg are the only callers. The product library never imports this
+package and shares no code with it.
+
+Functions take and return numpy arrays in the paged layout described in
+``paged_kv_cache_228_amd/workloads.py``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-std=c11", "-Wall"]
+
+
+def build_lib(force: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        build_lib()
+        L = C.CDLL(_LIB)
+        p, i32, i64, f32 = C.c_void_p, C.c_int, C.c_int64, C.c_float
+        L.pa_ref_half_to_float.argtypes = [C.c_uint16]
+        L.pa_ref_half_to_float.restype = f32
+        L.pa_ref_half_to_float_array.argtypes = [p, p, i64]
+        L.pa_ref_half_to_float_array.restype = None
+        L.pa_ref_max_threads.argtypes = []
+        L.pa_ref_max_threads.restype = i32
+        L.pa_ref_quantize_kv_int8.argtypes = [p, p, p, p, i64, i64, i32, i32, i32]
+        L.pa_ref_quantize_kv_int8.restype = i32
+        common = [p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, p, i32, p, i32]
+        L.pa_ref_paged_decode_f16.argtypes = [p, p, p] + common
+        L.pa_ref_paged_decode_f16.restype = i32
+        L.pa_ref_paged_decode_int8.argtypes = [p, p, p, p, p] + common
+        L.pa_ref_paged_decode_int8.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads() -> int:
+    return int(lib().pa_ref_max_threads())
+
+
+def half_to_float(bits: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns (uint16) -> float32 by the oracle's own decoder."""
+    b = _c(bits, np.uint16)
+    out = np.empty(b.shape, np.float32)
+    lib().pa_ref_half_to_float_array(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def quantize_kv_int8(pool: np.ndarray, block_ids=None):
+    """Quantize an fp16 pool ``[NB][H][B][d]``; returns (codes int8, scales f32 [NB][H]).
+    Blocks not listed in ``block_ids`` keep code 0 and scale 0."""
+    x = _c(pool, np.float16)
+    nb, h, bs, d = x.shape
+    codes = np.zeros(x.shape, np.int8)
+    scales = np.zeros((nb, h), np.float32)
+    ids = None if block_ids is None else _c(block_ids, np.int32)
+    rc = lib().pa_ref_quantize_kv_int8(_ptr(x.view(np.uint16)), _ptr(codes), _ptr(scales),
+                                       _ptr(ids), 0 if ids is None else ids.size, nb, h, bs, d)
+    if rc:
+        raise ValueError(f"oracle quantize failed ({rc})")
+    return codes, scales
+
+
+def _decode(fn, q, pools, tables, ctx, softmax_scale, num_blocks, seq_ids, want_weights):
+    q = _c(q, np.float16)
+    S, hq, d = q.shape
+    hkv, bs = pools[0].shape[1], pools[0].shape[2]
+    tables = _c(tables, np.int32)
+    ctx = _c(ctx, np.int32)
+    out = np.full((S, hq, d), np.nan, np.float32)
+    ids = None if seq_ids is None else _c(seq_ids, np.int32)
+    stride = max(1, int(ctx.max(initial=0)))
+    weights = np.full((S, hq, stride), np.nan, np.float32) if want_weights else None
+    rc = fn(_ptr(q.view(np.uint16)), *[_ptr(x) for x in pools], _ptr(tables), _ptr(ctx),
+            _ptr(out), S, hq, hkv, d, bs, tables.shape[1], num_blocks, float(softmax_scale),
+            _ptr(ids), 0 if ids is None else ids.size, _ptr(weights), stride)
+    if rc:
+        raise ValueError(f"oracle decode failed ({rc})")
+    return (out, weights) if want_weights else out
+
+
+def paged_decode_f16(q, k_pool, v_pool, block_tables, context_lens, softmax_scale,
+                     seq_ids=None, want_weights=False):
+    """fp32 output [S][H_q][d]; rows of sequences not in ``seq_ids`` stay NaN."""
+    k = _c(k_pool, np.float16).view(np.uint16)
+    v = _c(v_pool, np.float16).view(np.uint16)
+    return _decode(lib().pa_ref_paged_decode_f16, q, (k, v), block_tables, context_lens,
+                   softmax_scale, k.shape[0], seq_ids, want_weights)
+
+
+def paged_decode_int8(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens,
+                      softmax_scale, seq_ids=None, want_weights=False):
+    kc, vc = _c(k_codes, np.int8), _c(v_codes, np.int8)
+    ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    return _decode(lib().pa_ref_paged_decode_int8, q, (kc, vc, ks, vs), block_tables,
+                   context_lens, softmax_scale, kc.shape[0], seq_ids, want_weights)
+
+
+def decode_workload_f16(w, k_pool=None, v_pool=None, **kw):
+    return paged_decode_f16(w.q, w.k_pool if k_pool is None else k_pool,
+                            w.v_pool if v_pool is None else v_pool, w.block_tables,
+                            w.context_lens, w.softmax_scale, **kw)
+
+
+def decode_workload_int8(w, k_codes, v_codes, k_scale, v_scale, **kw):
+    return paged_decode_int8(w.q, k_codes, v_codes, k_scale, v_scale, w.block_tables,
+                             w.context_lens, w.softmax_scale, **kw)
