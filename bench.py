@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step runs the whole hot path once over one batch:
+  1. pa_quantize_kv_int8 on every live physical block (K and V),
+  2. pa_paged_decode_f16 over the fp16 cache,
+  3. pa_paged_decode_int8 over the INT8 cache just written.
+Each call is bracketed by its own HIP events on the stream it runs on.
+
+Default workload: pool of 65,536 blocks x 16 tokens, 64 sequences with
+context ~ U[512, 16384], 32 query heads / 8 KV heads, head_dim 128, groups of
+4 sequences sharing their first 64 physical blocks; q/K/V ~ N(0,1), seeded.
+
+Prints one JSON line. `value` is context (KV) tokens attended per second over
+the step (both decodes: 2 x sum(ctx) per step); the per-call figures, the
+roofline of the dominant call and the oracle's CPU time on the same step are
+in the same line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn tokens/sec + achieved HBM GB/s (% of peak), fp16 & INT8 KV"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixed_prefix",
+                    choices=["mixed_prefix", "int8_gaussian", "int8_heavy_tailed", "qwen2_s8",
+                             "tiny"])
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (CPU timing and output check)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path is "
+              "single-GPU by design, see the sharding notes in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_228_amd as pa
+    from paged_kv_cache_228_amd import workloads as W
+
+    pa.lib()  # fail loudly before any work if the library is missing
+    dev = torch.device("cuda:0")
+    t_gen = time.time()
+    w = {
+        "mixed_prefix": W.mixed_prefix,
+        "int8_gaussian": W.int8_gaussian,
+        "int8_heavy_tailed": W.int8_heavy_tailed,
+        "qwen2_s8": lambda: W.qwen2_layer(8),
+        "tiny": W.tiny,
+    }[args.workload]()
+    print(f"[bench] generated {w.name} in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, tables, ctx = up(w.q), up(w.block_tables), up(w.context_lens)
+    k16, v16 = up(w.k_pool), up(w.v_pool)
+    live = w.live_block_ids()
+    ids = up(live)
+    k8 = torch.zeros(k16.shape, dtype=torch.int8, device=dev)
+    v8 = torch.zeros_like(k8)
+    ks = torch.zeros(k16.shape[:2], dtype=torch.float32, device=dev)
+    vs = torch.zeros_like(ks)
+    out16 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    out8 = torch.empty_like(out16)
+    ws16 = pa.workspace_for(q, k16, tables, args.partition_tokens)
+    ws8 = pa.workspace_for(q, k8, tables, args.partition_tokens)
+    part = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq, 16,
+                                         args.partition_tokens)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        ev[0].record()
+        pa.pa_quantize_kv_int8(k16, v16, k8, v8, ks, vs, ids)
+        ev[1].record()
+        pa.pa_paged_decode_f16(q, k16, v16, tables, ctx, out16, w.softmax_scale,
+                               args.partition_tokens, ws16)
+        ev[2].record()
+        pa.pa_paged_decode_int8(q, k8, v8, ks, vs, tables, ctx, out8, w.softmax_scale,
+                                args.partition_tokens, ws8)
+        ev[3].record()
+
+    warm = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(1, args.warmup))]
+    for i in range(args.warmup):
+        step(warm[i])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+          for i, name in enumerate(["quantize", "fp16", "int8"])}
+    ms_step = wall * 1e3 / args.steps
+    sum_ctx = int(w.context_lens.sum())
+    S, d, hkv = w.num_seqs, w.head_dim, w.num_kv_heads
+    n_live = int(live.size)
+    alg = {
+        "fp16": W.algorithmic_bytes(w, 2, False),
+        "int8": W.algorithmic_bytes(w, 1, True),
+        # read fp16 K+V, write int8 K+V and two scales per (block, head), read the id list
+        "quantize": n_live * hkv * 16 * d * 2 * (2 + 1) + n_live * hkv * 2 * 4 + n_live * 4,
+    }
+    paths = {}
+    for name in ("quantize", "fp16", "int8"):
+        t = ms[name] * 1e-3
+        gbs = alg[name] / t / 1e9
+        rec = {"ms": round(ms[name], 5), "alg_bytes": alg[name], "gbs": round(gbs, 1),
+               "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        if name != "quantize":
+            rec["decode_tokens_per_s"] = round(S / t, 1)
+            rec["kv_tokens_per_s"] = round(sum_ctx / t, 1)
+        paths[name] = rec
+    dom = max(paths, key=lambda n: paths[n]["ms"])
+    call = {"quantize": "pa_quantize_kv_int8", "fp16": "pa_paged_decode_f16",
+            "int8": "pa_paged_decode_int8"}
+    roofline = {"bound": "hbm", "achieved": paths[dom]["gbs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": paths[dom]["frac_of_peak"], "traffic": None,
+                "kernel": call[dom]}
+
+    result = {
+        "metric": METRIC,
+        "value": round(2 * sum_ctx / (ms_step * 1e-3), 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16+int8 KV, fp32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": S, "sum_ctx": sum_ctx,
+            "ctx_min": int(w.context_lens.min()), "ctx_max": int(w.context_lens.max()),
+            "num_q_heads": w.num_q_heads, "num_kv_heads": hkv, "head_dim": d,
+            "block_size": 16, "pool_blocks": w.num_blocks, "live_blocks": n_live,
+            "partition_tokens": part,
+            "step": "quantize live blocks + fp16 decode + int8 decode",
+        },
+        "paths": paths,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        out16_h, out8_h = out16.cpu().numpy(), out8.cpu().numpy()
+        kc_h, vc_h, ks_h, vs_h = (x.cpu().numpy() for x in (k8, v8, ks, vs))
+        t0 = time.perf_counter()
+        okc, oks = oracle.quantize_kv_int8(w.k_pool, live)
+        ovc, ovs = oracle.quantize_kv_int8(w.v_pool, live)
+        t1 = time.perf_counter()
+        ref16 = oracle.decode_workload_f16(w)
+        t2 = time.perf_counter()
+        ref8 = oracle.decode_workload_int8(w, okc, ovc, oks, ovs)
+        t3 = time.perf_counter()
+        cpu_s = t3 - t0
+        result["cpu_baseline"] = {
+            "value": round(2 * sum_ctx / cpu_s, 1), "unit": "KV tokens/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": (f"one full step of the same batch: quantize of the {n_live} live blocks "
+                       f"({t1 - t0:.2f}s), fp16 decode ({t2 - t1:.2f}s), INT8 decode "
+                       f"({t3 - t2:.2f}s), all {S} sequences"),
+        }
+        result["parity"] = {
+            "codes_scales_bit_exact": bool(
+                np.array_equal(kc_h[live], okc[live]) and np.array_equal(vc_h[live], ovc[live])
+                and np.array_equal(ks_h[live].view(np.uint32), oks[live].view(np.uint32))
+                and np.array_equal(vs_h[live].view(np.uint32), ovs[live].view(np.uint32))),
+            "fp16_max_abs": float(np.max(np.abs(out16_h - ref16))),
+            "int8_max_abs": float(np.max(np.abs(out8_h - ref8))),
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,131 @@
+/*
+ * pa.h - paged single-token decode attention for AMD MI355X (gfx950).
+ *
+ * A K/V cache is split into fixed 16-token physical blocks; each sequence
+ * reaches its blocks through a block table, and one decode step attends a
+ * single query token per sequence over its whole context (paged-attention-
+ * runtime summary, "CORE CAPABILITIES" 1 "Block Manager" and 2 "CUDA Kernel":
+ * fixed 16-token blocks, block-table indirection, online single-pass softmax,
+ * fp32 accumulation; PagedKV-Fusion README, "Overview": per-(block, head)
+ * quantized decode attention).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is a DEVICE pointer owned by the caller. The library never
+ *    allocates, frees or synchronizes; each call enqueues its kernels on
+ *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *    returns without waiting. Calls keep no state and may be issued from
+ *    several host threads at once.
+ *  - K/V pools: [num_blocks][num_kv_heads][block_size][head_dim], row-major;
+ *    the 16 x head_dim tile of one (block, KV head) is contiguous. Token t of
+ *    sequence s lives in block block_tables[s][t / 16] at slot t % 16
+ *    (PagedAttention & KV-Cache glossary monograph, section 2.1).
+ *  - block_size must be 16; head_dim 64 or 128; num_q_heads a multiple of
+ *    num_kv_heads with num_q_heads / num_kv_heads between 1 and 8. Query head
+ *    h reads KV head h / (num_q_heads / num_kv_heads) (consecutive GQA
+ *    groups; paged-attention-runtime summary item 4, GQA expanded).
+ *  - q: fp16 [num_seqs][num_q_heads][head_dim]; out: fp32, same shape.
+ *    block_tables: int32 [num_seqs][max_blocks_per_seq]; context_lens: int32
+ *    [num_seqs]. q, pools, codes and out must be 16-byte aligned.
+ *  - Errors found on the host (NULL pointers, bad shapes, unsupported sizes,
+ *    a workspace that is too small) return a negative code before anything
+ *    is launched. A launch failure returns PA_ERR_HIP; pa_error_string then
+ *    names the HIP error. Device-resident data is not validated (that would
+ *    need a synchronization): a context length below 0 counts as 0 and one
+ *    above max_blocks_per_seq * 16 is clamped to it; a block id outside
+ *    [0, num_blocks) reads as a tile of zeros instead of faulting; a
+ *    sequence with context length 0 gets an all-zero output row.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL */
+    PA_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
+    PA_ERR_UNSUPPORTED = -3, /* valid but not built: block_size, head_dim, group size, alignment */
+    PA_ERR_WORKSPACE = -4,   /* split-K workspace missing or smaller than required */
+    PA_ERR_HIP = -5          /* a HIP call failed; see pa_error_string */
+};
+
+/* Static description of a return code. For PA_ERR_HIP it names the last HIP
+ * error seen by the calling thread. Never NULL. */
+const char* pa_error_string(int code);
+
+/* Symmetric INT8 quantization with one fp32 scale per (block, KV head), for
+ * K and for V separately (PagedKV-Fusion README, "Overview" and "Architecture":
+ * per-block,head symmetric INT8; "Memory footprint (exact arithmetic)": two
+ * fp32 scales per (block, head); glossary monograph section 5.1: code =
+ * round(x / S)). For every listed physical block b and KV head h, over the
+ * whole 16 x head_dim tile (unused slots included):
+ *     amax = max |x|,  scale = amax / 127 (fp32, IEEE-rounded division),
+ *     code = clamp(round_half_even(x / scale), -127, 127)  (x / scale an IEEE
+ *     fp32 division), and scale 0 gives codes 0.
+ *  k_f16, v_f16   in:  fp16 pools [num_blocks][num_kv_heads][16][head_dim]
+ *  k_i8, v_i8     out: int8 code pools of the same shape
+ *  k_scale,v_scale out: fp32 [num_blocks][num_kv_heads]
+ *  block_ids      in:  int32 [num_ids] physical blocks to quantize, or NULL for
+ *                      all num_blocks blocks; other blocks are left untouched.
+ *                      Ids outside [0, num_blocks) are skipped on the device.
+ * Returns PA_OK or a negative PA_ERR_* code. */
+int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8_t* v_i8,
+                        float* k_scale, float* v_scale, const int32_t* block_ids,
+                        int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                        int head_dim, void* stream);
+
+/* Bytes of split-K workspace a decode call with these sizes needs (0 when the
+ * context fits one partition). partition_tokens: tokens per context partition,
+ * a multiple of 16, or 0 to let the library choose; partitions are capped at
+ * 4096 tokens. Returns 0 for arguments the decode calls would reject. */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_blocks_per_seq, int block_size, int partition_tokens);
+
+/* Tokens per context partition the decode calls will use for these sizes
+ * (the library's choice when partition_tokens is 0), or a negative PA_ERR_*
+ * code for arguments the decode calls would reject. */
+int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
+                               int block_size, int partition_tokens);
+
+/* Decode attention over an fp16 paged KV cache. For every sequence s and
+ * query head h, with n = context_lens[s] and k_t, v_t the K/V rows of token t
+ * reached through the block table:
+ *     out[s][h] = sum_t softmax_t(softmax_scale * q[s][h] . k_t) * v_t
+ * computed with a single-pass online softmax in fp32 (paged-attention-runtime
+ * summary, "CORE CAPABILITIES" 2; glossary monograph section 5.2,
+ * softmax(Q K^T / sqrt(d))). Long contexts are split into partitions whose
+ * partial results are merged by a second, stream-ordered kernel; workspace
+ * must then hold pa_decode_workspace_bytes(...) bytes (it may be NULL when
+ * that is 0). num_seqs may be 0 (nothing is launched). */
+int pa_paged_decode_f16(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, float* out,
+                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                        float softmax_scale, int partition_tokens, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Same as pa_paged_decode_f16 over an INT8 cache produced by
+ * pa_quantize_kv_int8: K and V elements are float(code) * scale of their
+ * (block, KV head), dequantized in registers (PagedKV-Fusion README,
+ * "Overview": per-(block, head) quantized decode attention).
+ *  k_cache, v_cache: int8 [num_blocks][num_kv_heads][16][head_dim]
+ *  k_scale, v_scale: fp32 [num_blocks][num_kv_heads] */
+int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens, float* out,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                         float softmax_scale, int partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

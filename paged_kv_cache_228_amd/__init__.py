@@ -1,0 +1,213 @@
+"""Paged single-token decode attention for AMD MI355X (gfx950).
+
+Python binding of the C-ABI library ``libpa.so`` (declared in
+``include/pa.h``). The functions below have the library's names and only
+marshal arguments: shapes are read off torch tensors, pointers and the
+current HIP stream are passed through, and a non-zero return code raises
+``PagedAttentionError``. Every step of the computation runs in the library's
+HIP kernels; there is no fallback. If ``libpa.so`` is missing the first call
+raises, naming the build command.
+
+Tensor layouts (all on the GPU, contiguous):
+  q            fp16  [num_seqs][num_q_heads][head_dim]
+  k/v cache    fp16 or int8 [num_blocks][num_kv_heads][16][head_dim]
+  k/v scale    fp32  [num_blocks][num_kv_heads]
+  block_tables int32 [num_seqs][max_blocks_per_seq]
+  context_lens int32 [num_seqs]
+  out          fp32  [num_seqs][num_q_heads][head_dim]
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK = 0
+PA_ERR_NULL = -1
+PA_ERR_SHAPE = -2
+PA_ERR_UNSUPPORTED = -3
+PA_ERR_WORKSPACE = -4
+PA_ERR_HIP = -5
+
+EXPORTED = (
+    "pa_error_string",
+    "pa_quantize_kv_int8",
+    "pa_decode_workspace_bytes",
+    "pa_decode_partition_tokens",
+    "pa_paged_decode_f16",
+    "pa_paged_decode_int8",
+)
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed with {code}: {pa_error_string(code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libpa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m paged_kv_cache_228_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+        L.pa_error_string.argtypes = [i32]
+        L.pa_error_string.restype = C.c_char_p
+        L.pa_quantize_kv_int8.argtypes = [p, p, p, p, p, p, p, i64, i64, i32, i32, i32, p]
+        L.pa_quantize_kv_int8.restype = i32
+        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.pa_decode_workspace_bytes.restype = sz
+        L.pa_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32]
+        L.pa_decode_partition_tokens.restype = i32
+        tail = [p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, i32, p, sz, p]
+        L.pa_paged_decode_f16.argtypes = [p, p, p] + tail
+        L.pa_paged_decode_f16.restype = i32
+        L.pa_paged_decode_int8.argtypes = [p, p, p, p, p] + tail
+        L.pa_paged_decode_int8.restype = i32
+        _lib = L
+    return _lib
+
+
+def pa_error_string(code: int) -> str:
+    return lib().pa_error_string(int(code)).decode()
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return C.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+    import torch
+
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pa_quantize_kv_int8(k_f16, v_f16, k_i8, v_i8, k_scale, v_scale, block_ids=None, stream=None):
+    """Quantize fp16 K/V pools to INT8 codes plus one fp32 scale per (block, head)."""
+    import torch
+
+    for t, n in ((k_f16, "k_f16"), (v_f16, "v_f16")):
+        _need(t, n, torch.float16, 4)
+    for t, n in ((k_i8, "k_i8"), (v_i8, "v_i8")):
+        _need(t, n, torch.int8, 4)
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, n, torch.float32, 2)
+    nb, hkv, bs, d = k_f16.shape
+    nids = 0
+    if block_ids is not None:
+        _need(block_ids, "block_ids", torch.int32, 1)
+        nids = block_ids.numel()
+    rc = lib().pa_quantize_kv_int8(_ptr(k_f16), _ptr(v_f16), _ptr(k_i8), _ptr(v_i8),
+                                   _ptr(k_scale), _ptr(v_scale), _ptr(block_ids), nids, nb, hkv,
+                                   bs, d, _stream(k_f16, stream))
+    if rc:
+        raise PagedAttentionError("pa_quantize_kv_int8", rc)
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                              block_size=16, partition_tokens=0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_blocks_per_seq, block_size, partition_tokens))
+
+
+def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq, block_size=16,
+                               partition_tokens=0) -> int:
+    r = int(lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq,
+                                             block_size, partition_tokens))
+    if r < 0:
+        raise PagedAttentionError("pa_decode_partition_tokens", r)
+    return r
+
+
+def workspace_for(q, k_cache, block_tables, partition_tokens=0):
+    """A torch byte buffer of the size the decode calls need (None if none)."""
+    import torch
+
+    n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
+                                  block_tables.shape[1], k_cache.shape[2], partition_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+
+
+def _decode_args(q, k_cache, block_tables, context_lens, out):
+    import torch
+
+    _need(q, "q", torch.float16, 3)
+    _need(out, "out", torch.float32, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_tables / context_lens rows must match num_seqs")
+    nb, hkv, bs, d = k_cache.shape
+    if d != q.shape[2]:
+        raise ValueError("head_dim of q and cache differ")
+    return q.shape[0], q.shape[1], hkv, d, bs, block_tables.shape[1], nb
+
+
+def pa_paged_decode_f16(q, k_cache, v_cache, block_tables, context_lens, out, softmax_scale,
+                        partition_tokens=0, workspace=None, stream=None):
+    """Decode attention over an fp16 paged cache; writes ``out``."""
+    import torch
+
+    _need(k_cache, "k_cache", torch.float16, 4)
+    _need(v_cache, "v_cache", torch.float16, 4)
+    S, hq, hkv, d, bs, mb, nb = _decode_args(q, k_cache, block_tables, context_lens, out)
+    if workspace is None:
+        workspace = workspace_for(q, k_cache, block_tables, partition_tokens)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_paged_decode_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(context_lens), _ptr(out), S, hq, hkv, d, bs, mb, nb,
+                                   float(softmax_scale), int(partition_tokens), _ptr(workspace),
+                                   wbytes, _stream(q, stream))
+    if rc:
+        raise PagedAttentionError("pa_paged_decode_f16", rc)
+
+
+def pa_paged_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                         softmax_scale, partition_tokens=0, workspace=None, stream=None):
+    """Decode attention over an INT8 paged cache with per-(block, head) scales."""
+    import torch
+
+    _need(k_cache, "k_cache", torch.int8, 4)
+    _need(v_cache, "v_cache", torch.int8, 4)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    _need(v_scale, "v_scale", torch.float32, 2)
+    S, hq, hkv, d, bs, mb, nb = _decode_args(q, k_cache, block_tables, context_lens, out)
+    if workspace is None:
+        workspace = workspace_for(q, k_cache, block_tables, partition_tokens)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_paged_decode_int8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                    _ptr(out), S, hq, hkv, d, bs, mb, nb, float(softmax_scale),
+                                    int(partition_tokens), _ptr(workspace), wbytes,
+                                    _stream(q, stream))
+    if rc:
+        raise PagedAttentionError("pa_paged_decode_int8", rc)
+
+
+__all__ = [
+    "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
+    "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
+    "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8",
+]

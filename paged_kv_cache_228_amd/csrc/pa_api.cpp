@@ -1,0 +1,215 @@
+// C-ABI front end of the paged decode attention library: argument checks,
+// partition sizing and kernel launches. Declarations and the contract of each
+// call are in include/pa.h.
+#include "pa.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_hip_msg[160] = "no HIP error recorded";
+
+int hip_fail(hipError_t e)
+{
+    std::snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return PA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Partition size in blocks. An explicit request is honoured up to the
+// 256-block staging limit. Otherwise the largest of 32, 16, 8, 4 blocks
+// (512 .. 64 tokens) that still gives at least 2048 workgroups for the
+// longest possible context, so the 256 compute units each get several.
+int choose_part_blocks(int num_seqs, int num_kv_heads, int max_blocks, int partition_tokens)
+{
+    int pb;
+    if (partition_tokens > 0) {
+        pb = partition_tokens / pa::kBlockTokens;
+    } else {
+        pb = 4;
+        const long long units = (long long)num_seqs * num_kv_heads;
+        for (int cand : {32, 16, 8}) {
+            const long long parts = (max_blocks + cand - 1) / cand;
+            if (units * parts >= 2048) {
+                pb = cand;
+                break;
+            }
+        }
+    }
+    if (pb > pa::kMaxPartitionBlocks) pb = pa::kMaxPartitionBlocks;
+    if (pb > max_blocks) pb = max_blocks;
+    if (pb < 1) pb = 1;
+    return pb;
+}
+
+int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                       int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                       int partition_tokens)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || partition_tokens < 0)
+        return PA_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads) return PA_ERR_SHAPE;
+    if (partition_tokens % pa::kBlockTokens) return PA_ERR_SHAPE;
+    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    const int group = num_q_heads / num_kv_heads;
+    if (group < 1 || group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * pa::kBlockTokens > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int decode_common(const void* q, const void* k, const void* v, const float* ks, const float* vs,
+                  const int32_t* tables, const int32_t* ctx, float* out, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                  int max_blocks_per_seq, int64_t num_blocks, float softmax_scale,
+                  int partition_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                  bool int8)
+{
+    if (!q || !k || !v || !tables || !ctx || !out) return PA_ERR_NULL;
+    if (int8 && (!ks || !vs)) return PA_ERR_NULL;
+    int rc = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, partition_tokens);
+    if (rc) return rc;
+    if (!std::isfinite(softmax_scale)) return PA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+
+    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens);
+    const int parts = (max_blocks_per_seq + pb - 1) / pb;
+    if (parts > 1) {
+        const size_t need = pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
+        if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    }
+    if (parts > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+
+    pa::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.k_scale = ks;
+    a.v_scale = vs;
+    a.tables = tables;
+    a.ctx = ctx;
+    a.out = out;
+    a.ws = static_cast<float*>(workspace);
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.part_blocks = pb;
+    a.max_parts = parts;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, int8,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_error_string(int code)
+{
+    switch (code) {
+        case PA_OK: return "success";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_SHAPE: return "inconsistent or non-positive sizes";
+        case PA_ERR_UNSUPPORTED:
+            return "unsupported configuration (block_size must be 16, head_dim 64 or 128, "
+                   "1..8 query heads per KV head, 16-byte aligned buffers)";
+        case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
+        case PA_ERR_HIP: return g_hip_msg;
+        default: return "unknown error code";
+    }
+}
+
+int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8_t* v_i8,
+                        float* k_scale, float* v_scale, const int32_t* block_ids,
+                        int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                        int head_dim, void* stream)
+{
+    if (!k_f16 || !v_f16 || !k_i8 || !v_i8 || !k_scale || !v_scale) return PA_ERR_NULL;
+    if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+        return PA_ERR_SHAPE;
+    if (block_ids && num_ids < 0) return PA_ERR_SHAPE;
+    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_f16) || !aligned16(v_f16) || (reinterpret_cast<uintptr_t>(k_i8) & 7u) ||
+        (reinterpret_cast<uintptr_t>(v_i8) & 7u))
+        return PA_ERR_UNSUPPORTED;
+    pa::QuantArgs a;
+    a.k = static_cast<const uint16_t*>(k_f16);
+    a.v = static_cast<const uint16_t*>(v_f16);
+    a.kc = k_i8;
+    a.vc = v_i8;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.ids = block_ids;
+    a.num_ids = block_ids ? num_ids : num_blocks;
+    a.num_blocks = num_blocks;
+    a.num_kv_heads = num_kv_heads;
+    if ((a.num_ids * num_kv_heads * 2 + 3) / 4 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    hipError_t e = pa::launch_quantize(a, head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
+int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
+                               int block_size, int partition_tokens)
+{
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
+        partition_tokens < 0 || partition_tokens % pa::kBlockTokens)
+        return PA_ERR_SHAPE;
+    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+    return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens) *
+           pa::kBlockTokens;
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                 int max_blocks_per_seq, int block_size, int partition_tokens)
+{
+    if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, 1, partition_tokens))
+        return 0;
+    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens);
+    const int parts = (max_blocks_per_seq + pb - 1) / pb;
+    if (parts <= 1) return 0;
+    return pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
+}
+
+int pa_paged_decode_f16(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, float* out,
+                        int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                        int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                        float softmax_scale, int partition_tokens, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
+                         workspace, workspace_bytes, stream, false);
+}
+
+int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens, float* out,
+                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                         int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                         float softmax_scale, int partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
+                         workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"

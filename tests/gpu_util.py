@@ -1,0 +1,84 @@
+"""Helpers shared by the GPU tests: move a workload to the device, call the
+library through its Python binding, bring results back. Torch is used only
+for device memory and streams."""
+
+import numpy as np
+
+import paged_kv_cache_228_amd as pa
+from paged_kv_cache_228_amd import workloads as W
+
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+
+
+def dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def quantize(k_pool, v_pool, block_ids=None):
+    """GPU quantization of two fp16 pools; returns numpy (kc, vc, ks, vs)."""
+    import torch
+
+    k, v = dev(k_pool), dev(v_pool)
+    kc = torch.zeros(k.shape, dtype=torch.int8, device=DEV)
+    vc = torch.zeros(v.shape, dtype=torch.int8, device=DEV)
+    ks = torch.zeros(k.shape[:2], dtype=torch.float32, device=DEV)
+    vs = torch.zeros(v.shape[:2], dtype=torch.float32, device=DEV)
+    ids = None if block_ids is None else dev(np.asarray(block_ids, np.int32))
+    pa.pa_quantize_kv_int8(k, v, kc, vc, ks, vs, ids)
+    sync()
+    return kc.cpu().numpy(), vc.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy()
+
+
+def decode_f16(w: W.Workload, k_pool=None, v_pool=None, tables=None, ctx=None,
+               partition_tokens=0, num_blocks=None):
+    import torch
+
+    k = dev(w.k_pool if k_pool is None else k_pool)
+    v = dev(w.v_pool if v_pool is None else v_pool)
+    if num_blocks is not None:  # expose only the first num_blocks blocks
+        k, v = k[:num_blocks], v[:num_blocks]
+    q = dev(w.q)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    pa.pa_paged_decode_f16(q, k, v, dev(w.block_tables if tables is None else tables),
+                           dev(w.context_lens if ctx is None else ctx), out, w.softmax_scale,
+                           partition_tokens)
+    sync()
+    return out.cpu().numpy()
+
+
+def decode_int8(w: W.Workload, kc, vc, ks, vs, tables=None, ctx=None, partition_tokens=0,
+                num_blocks=None):
+    import torch
+
+    kc, vc, ks, vs = dev(kc), dev(vc), dev(ks), dev(vs)
+    if num_blocks is not None:
+        kc, vc, ks, vs = kc[:num_blocks], vc[:num_blocks], ks[:num_blocks], vs[:num_blocks]
+    q = dev(w.q)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    pa.pa_paged_decode_int8(q, kc, vc, ks, vs, dev(w.block_tables if tables is None else tables),
+                            dev(w.context_lens if ctx is None else ctx), out, w.softmax_scale,
+                            partition_tokens)
+    sync()
+    return out.cpu().numpy()
+
+
+def poison_codes(w: W.Workload, codes: np.ndarray) -> np.ndarray:
+    """Copy of an INT8 code pool with +-127 in every dead slot (proves masking)."""
+    out = codes.copy()
+    view = out.transpose(0, 2, 1, 3)  # [NB][16][H][d]
+    dead = w.dead_slot_mask()
+    pattern = np.where(np.arange(out.shape[3]) % 2 == 0, 127, -127).astype(np.int8)
+    view[dead] = pattern
+    return out

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bars: INT8 codes and scales bit-exact; fp16-path outputs within max-abs 2e-3
+of the oracle; INT8-path outputs within max-abs 1e-3 of the oracle's own
+dequantized computation. Every workload is compared in full (every output
+element), the full-size ones included.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_228_amd import workloads as W
+
+from gpu_util import decode_f16, decode_int8, poison_codes, quantize, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_F16 = 2e-3
+TOL_I8 = 1e-3
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name: str) -> W.Workload:
+    say(f"generating {name}")
+    return {
+        "tiny": W.tiny,
+        "qwen2_s1": lambda: W.qwen2_layer(1),
+        "qwen2_s4": lambda: W.qwen2_layer(4),
+        "qwen2_s8": lambda: W.qwen2_layer(8),
+        "int8_gaussian": W.int8_gaussian,
+        "int8_heavy_tailed": W.int8_heavy_tailed,
+        "mixed_prefix": W.mixed_prefix,
+    }[name]()
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_codes(name: str):
+    w = workload(name)
+    ids = w.live_block_ids() if name == "mixed_prefix" else None
+    kc, ks = oracle.quantize_kv_int8(w.k_pool, ids)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool, ids)
+    return ids, kc, vc, ks, vs
+
+
+ALL = ["tiny", "qwen2_s1", "qwen2_s4", "qwen2_s8", "int8_gaussian", "int8_heavy_tailed",
+       "mixed_prefix"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_quantize_bit_exact(name):
+    w = workload(name)
+    ids, kc, vc, ks, vs = oracle_codes(name)
+    say(f"quantize {name} blocks={w.num_blocks} ids={'all' if ids is None else len(ids)}")
+    gkc, gvc, gks, gvs = quantize(w.k_pool, w.v_pool, ids)
+    assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(gvs.view(np.uint32), vs.view(np.uint32))
+    assert np.array_equal(gkc, kc)
+    assert np.array_equal(gvc, vc)
+
+
+def test_quantize_exhaustive_over_all_finite_fp16():
+    """Every finite fp16 value x, quantized in tiles whose amax is one of several
+    values (x kept only when |x| <= amax), matches the oracle bit for bit."""
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = bits.view(np.float16)
+    finite = vals[np.isfinite(vals)]
+    assert finite.size == 63488
+    tiles = []
+    for amax in (65504.0, 1000.0, 127.0, 3.140625, 1.0, 0.0999, 6.1e-5, 5.96e-8):
+        a = np.float16(amax)
+        xs = finite[np.abs(finite.astype(np.float32)) <= np.float32(a)]
+        per = 16 * 64 - 1
+        for i in range(0, xs.size, per):
+            t = np.zeros(16 * 64, np.float16)
+            t[0] = a
+            chunk = xs[i : i + per]
+            t[1 : 1 + chunk.size] = chunk
+            tiles.append(t.reshape(16, 64))
+    pool = np.stack(tiles)[:, None]  # [n][1][16][64]
+    say(f"exhaustive quantize sweep tiles={pool.shape[0]}")
+    kc, ks = oracle.quantize_kv_int8(pool)
+    gkc, gvc, gks, gvs = quantize(pool, pool[::-1].copy())
+    assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(gkc, kc)
+    assert np.array_equal(gvc, kc[::-1])
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_decode_f16_matches_oracle(name):
+    w = workload(name)
+    kp, vp = w.poisoned(w.k_pool), w.poisoned(w.v_pool)
+    say(f"decode f16 {name} S={w.num_seqs} ctx_sum={int(w.context_lens.sum())}")
+    out = decode_f16(w, kp, vp)
+    ref = oracle.decode_workload_f16(w)
+    assert np.isfinite(out).all()
+    err = float(np.max(np.abs(out - ref)))
+    say(f"decode f16 {name} max_abs={err:.3e}")
+    assert err <= TOL_F16
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_decode_int8_matches_oracle(name):
+    w = workload(name)
+    ids, kc, vc, ks, vs = oracle_codes(name)
+    kcp, vcp = poison_codes(w, kc), poison_codes(w, vc)
+    say(f"decode int8 {name} S={w.num_seqs}")
+    out = decode_int8(w, kcp, vcp, ks, vs)
+    ref = oracle.decode_workload_int8(w, kc, vc, ks, vs)
+    assert np.isfinite(out).all()
+    err = float(np.max(np.abs(out - ref)))
+    say(f"decode int8 {name} max_abs={err:.3e}")
+    assert err <= TOL_I8
+
+
+def _ragged():
+    return W.build("ragged", 501, [1, 15, 16, 17, 100, 513, 2000, 4100, 0, 33], 8, 2, 128,
+                   num_blocks=600)
+
+
+@pytest.mark.parametrize("path", ["f16", "int8"])
+def test_partition_size_invariance(path):
+    w = _ragged()
+    if path == "int8":
+        kc, ks = oracle.quantize_kv_int8(w.k_pool)
+        vc, vs = oracle.quantize_kv_int8(w.v_pool)
+        ref = oracle.decode_workload_int8(w, kc, vc, ks, vs)
+        run = lambda p: decode_int8(w, kc, vc, ks, vs, partition_tokens=p)  # noqa: E731
+        tol = TOL_I8
+    else:
+        ref = oracle.decode_workload_f16(w)
+        run = lambda p: decode_f16(w, w.poisoned(w.k_pool), w.poisoned(w.v_pool),  # noqa: E731
+                                   partition_tokens=p)
+        tol = TOL_F16
+    outs = {}
+    for p in (16, 48, 64, 256, 512, 4096, 0):
+        say(f"partition {path} tokens={p}")
+        outs[p] = run(p)
+        assert np.max(np.abs(outs[p] - ref)) <= tol
+    for p, o in outs.items():
+        assert np.max(np.abs(o - outs[4096])) <= 1e-5, p
+    assert not outs[0][8].any()  # the empty sequence
+
+
+@pytest.mark.parametrize("path", ["f16", "int8"])
+def test_block_permutation_invariance_is_bitwise(path):
+    w = W.build("perm", 502, [70, 333, 16, 1000], 8, 2, 64, num_blocks=120)
+    perm = np.random.default_rng(9).permutation(w.num_blocks).astype(np.int32)
+    t2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    k2, v2 = np.empty_like(w.k_pool), np.empty_like(w.v_pool)
+    k2[perm], v2[perm] = w.k_pool, w.v_pool
+    say(f"permutation {path}")
+    if path == "f16":
+        a = decode_f16(w)
+        b = decode_f16(w, k2, v2, tables=t2)
+    else:
+        kc, ks = oracle.quantize_kv_int8(w.k_pool)
+        vc, vs = oracle.quantize_kv_int8(w.v_pool)
+        kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+        ks2, vs2 = np.empty_like(ks), np.empty_like(vs)
+        kc2[perm], vc2[perm], ks2[perm], vs2[perm] = kc, vc, ks, vs
+        a = decode_int8(w, kc, vc, ks, vs)
+        b = decode_int8(w, kc2, vc2, ks2, vs2, tables=t2)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_every_group_size_and_head_dim(g, d):
+    w = W.build(f"g{g}d{d}", 600 + 10 * g + d, [5, 77, 300, 16], 2 * g, 2, d, num_blocks=40)
+    say(f"group {g} head_dim {d}")
+    out = decode_f16(w, w.poisoned(w.k_pool), w.poisoned(w.v_pool))
+    ref = oracle.decode_workload_f16(w)
+    assert np.max(np.abs(out - ref)) <= TOL_F16
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    out8 = decode_int8(w, poison_codes(w, kc), poison_codes(w, vc), ks, vs)
+    ref8 = oracle.decode_workload_int8(w, kc, vc, ks, vs)
+    assert np.max(np.abs(out8 - ref8)) <= TOL_I8
+
+
+def test_edge_context_lengths():
+    """ctx 0 gives zeros; negative counts as 0; lengths past the table are
+    clamped to max_blocks_per_seq * 16."""
+    w = W.build("edge", 700, [0, 1, 16, 17, 64], 4, 2, 64, num_blocks=12)
+    ctx = w.context_lens.copy()
+    ctx[0] = -5
+    ctx[4] = 10_000  # clamps to 4 blocks = 64 tokens, the real length
+    say("edge contexts")
+    out = decode_f16(w, ctx=ctx)
+    ref = oracle.decode_workload_f16(w)
+    assert not out[0].any()
+    assert np.max(np.abs(out - ref)) <= TOL_F16
+    # ctx 1: exactly the single value row (softmax weight 1)
+    b = w.block_tables[1, 0]
+    assert np.max(np.abs(out[1] - np.repeat(w.v_pool[b, :, 0].astype(np.float32), 2, 0))) <= 1e-6
+
+
+def test_out_of_range_block_ids_read_as_zero_tiles():
+    w = W.build("oob", 701, [40, 20], 4, 2, 64, num_blocks=6)
+    t = w.block_tables.copy()
+    t[0, 1] = 6  # == num_blocks: outside the pool
+    t[1, 0] = -7
+    # oracle: a pool with an extra all-zero block 6, and -7 redirected to it
+    kz = np.concatenate([w.k_pool, np.zeros_like(w.k_pool[:1])])
+    vz = np.concatenate([w.v_pool, np.zeros_like(w.v_pool[:1])])
+    tz = np.where(t < 0, 6, t).astype(np.int32)
+    ref = oracle.paged_decode_f16(w.q, kz, vz, tz, w.context_lens, w.softmax_scale)
+    say("out-of-range block ids")
+    out = decode_f16(w, tables=t)
+    assert np.max(np.abs(out - ref)) <= TOL_F16
+    kc, ks = oracle.quantize_kv_int8(kz)
+    vc, vs = oracle.quantize_kv_int8(vz)
+    ref8 = oracle.paged_decode_int8(w.q, kc, vc, ks, vs, tz, w.context_lens, w.softmax_scale)
+    out8 = decode_int8(w, kc, vc, ks, vs, tables=t, num_blocks=6)
+    assert np.max(np.abs(out8 - ref8)) <= TOL_I8
+
+
+@pytest.mark.parametrize("name", ["int8_gaussian", "int8_heavy_tailed"])
+def test_int8_error_against_fp32_is_reported(name):
+    """INT8-versus-fp32 quality on the GPU path (the fp32 reference is the
+    oracle on the fp16-stored K/V), reported like the pages' quality table."""
+    w = workload(name)
+    ids, kc, vc, ks, vs = oracle_codes(name)
+    ref = oracle.decode_workload_f16(w).astype(np.float64)
+    out = decode_int8(w, kc, vc, ks, vs).astype(np.float64)
+    rmse = float(np.sqrt(np.mean((out - ref) ** 2)))
+    mx = float(np.max(np.abs(out - ref)))
+    say(f"{name}: INT8 vs FP32 rmse={rmse:.5f} max_abs={mx:.4f} fp32_out_std={ref.std():.4f}")
+    assert np.isfinite(rmse)
+    if name == "int8_gaussian":
+        assert rmse < 1e-2
