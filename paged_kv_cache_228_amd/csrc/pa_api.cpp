@@ -88,7 +88,7 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
         const size_t need = pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
         if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     }
-    if (parts > 0x7fffffff) return PA_ERR_UNSUPPORTED;
+    if (parts > 65535) return PA_ERR_UNSUPPORTED;  // one grid dimension per partition index
 
     pa::DecodeArgs a;
     a.q = q;

@@ -414,39 +414,60 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a)
 }
 
 template <int D, int G, bool I8>
-hipError_t launch_one(const DecodeArgs& a, hipStream_t st)
+hipError_t launch_valu(const DecodeArgs& a, hipStream_t st)
 {
     const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
     hipLaunchKernelGGL((decode_partition_kernel<D, G, I8>), grid, dim3(kThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_parts <= 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D, bool I8>
-hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t st)
+hipError_t launch_valu_d(const DecodeArgs& a, int group, hipStream_t st)
 {
     switch (group) {
-        case 1: return launch_one<D, 1, I8>(a, st);
-        case 2: return launch_one<D, 2, I8>(a, st);
-        case 3: return launch_one<D, 3, I8>(a, st);
-        case 4: return launch_one<D, 4, I8>(a, st);
-        case 5: return launch_one<D, 5, I8>(a, st);
-        case 6: return launch_one<D, 6, I8>(a, st);
-        case 7: return launch_one<D, 7, I8>(a, st);
-        case 8: return launch_one<D, 8, I8>(a, st);
+        case 1: return launch_valu<D, 1, I8>(a, st);
+        case 2: return launch_valu<D, 2, I8>(a, st);
+        case 3: return launch_valu<D, 3, I8>(a, st);
+        case 4: return launch_valu<D, 4, I8>(a, st);
+        case 5: return launch_valu<D, 5, I8>(a, st);
+        case 6: return launch_valu<D, 6, I8>(a, st);
+        case 7: return launch_valu<D, 7, I8>(a, st);
+        case 8: return launch_valu<D, 8, I8>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+// Partition kernel on the vector ALUs (one four-wave workgroup per
+// partition, every lane reducing its own dims); kept for comparison with the
+// matrix-core kernel.
+hipError_t launch_decode_partitions_valu(const DecodeArgs& a, int head_dim, int group, bool int8,
+                                         hipStream_t st)
+{
+    if (head_dim == 64) return int8 ? launch_valu_d<64, true>(a, group, st) : launch_valu_d<64, false>(a, group, st);
+    if (head_dim == 128) return int8 ? launch_valu_d<128, true>(a, group, st) : launch_valu_d<128, false>(a, group, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st)
+{
+    const dim3 grid(a.num_q_heads, a.num_seqs);
+    if (head_dim == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, st, a);
+    else if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(64), 0, st, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st)
 {
-    if (head_dim == 64) return int8 ? launch_d<64, true>(a, group, st) : launch_d<64, false>(a, group, st);
-    if (head_dim == 128) return int8 ? launch_d<128, true>(a, group, st) : launch_d<128, false>(a, group, st);
-    return hipErrorInvalidValue;
+#ifdef PA_DECODE_VALU
+    hipError_t e = launch_decode_partitions_valu(a, head_dim, group, int8, st);
+#else
+    hipError_t e = launch_decode_partitions_mfma(a, head_dim, group, int8, st);
+#endif
+    if (e != hipSuccess || a.max_parts <= 1) return e;
+    return launch_decode_merge(a, head_dim, st);
 }
 
 }  // namespace pa

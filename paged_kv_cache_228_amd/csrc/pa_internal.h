@@ -39,7 +39,13 @@ inline size_t workspace_floats(int S, int Hq, int P, int D)
     return (size_t)S * Hq * P * (size_t)(D + 2);
 }
 
+// Partition kernel + (when max_parts > 1) the split-K merge kernel.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st);
+hipError_t launch_decode_partitions_mfma(const DecodeArgs& a, int head_dim, int group, bool int8,
+                                         hipStream_t st);
+hipError_t launch_decode_partitions_valu(const DecodeArgs& a, int head_dim, int group, bool int8,
+                                         hipStream_t st);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
 
 struct QuantArgs {
     const uint16_t* k;
