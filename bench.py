@@ -81,8 +81,9 @@ def main() -> int:
     out8 = torch.empty_like(out16)
     ws16 = pa.workspace_for(q, k16, tables, args.partition_tokens)
     ws8 = pa.workspace_for(q, k8, tables, args.partition_tokens)
-    part = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq, 16,
-                                         args.partition_tokens)
+    part = {name: pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq,
+                                                16, args.partition_tokens, kv_int8=i8)
+            for name, i8 in (("fp16", False), ("int8", True))}
     torch.cuda.synchronize()
 
     def step(ev):

@@ -83,15 +83,19 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
 /* Bytes of split-K workspace a decode call with these sizes needs (0 when the
  * context fits one partition). partition_tokens: tokens per context partition,
  * a multiple of 16, or 0 to let the library choose; partitions are capped at
- * 4096 tokens. Returns 0 for arguments the decode calls would reject. */
+ * 4096 tokens. kv_int8: 0 for pa_paged_decode_f16, nonzero for
+ * pa_paged_decode_int8 (the automatic partition size depends on the KV
+ * dtype). Returns 0 for arguments the decode calls would reject. */
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_blocks_per_seq, int block_size, int partition_tokens);
+                                 int max_blocks_per_seq, int block_size, int partition_tokens,
+                                 int kv_int8);
 
-/* Tokens per context partition the decode calls will use for these sizes
- * (the library's choice when partition_tokens is 0), or a negative PA_ERR_*
- * code for arguments the decode calls would reject. */
+/* Tokens per context partition the decode call for this KV dtype (kv_int8 as
+ * above) will use for these sizes (the library's choice when
+ * partition_tokens is 0), or a negative PA_ERR_* code for arguments the
+ * decode calls would reject. */
 int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
-                               int block_size, int partition_tokens);
+                               int block_size, int partition_tokens, int kv_int8);
 
 /* Decode attention over an fp16 paged KV cache. For every sequence s and
  * query head h, with n = context_lens[s] and k_t, v_t the K/V rows of token t

@@ -64,9 +64,9 @@ def lib() -> C.CDLL:
         L.pa_error_string.restype = C.c_char_p
         L.pa_quantize_kv_int8.argtypes = [p, p, p, p, p, p, p, i64, i64, i32, i32, i32, p]
         L.pa_quantize_kv_int8.restype = i32
-        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_workspace_bytes.restype = sz
-        L.pa_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32]
+        L.pa_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32]
         L.pa_decode_partition_tokens.restype = i32
         tail = [p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, i32, p, sz, p]
         L.pa_paged_decode_f16.argtypes = [p, p, p] + tail
@@ -125,26 +125,29 @@ def pa_quantize_kv_int8(k_f16, v_f16, k_i8, v_i8, k_scale, v_scale, block_ids=No
 
 
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                              block_size=16, partition_tokens=0) -> int:
+                              block_size=16, partition_tokens=0, kv_int8=False) -> int:
     return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                               max_blocks_per_seq, block_size, partition_tokens))
+                                               max_blocks_per_seq, block_size, partition_tokens,
+                                               int(bool(kv_int8))))
 
 
 def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq, block_size=16,
-                               partition_tokens=0) -> int:
+                               partition_tokens=0, kv_int8=False) -> int:
     r = int(lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq,
-                                             block_size, partition_tokens))
+                                             block_size, partition_tokens, int(bool(kv_int8))))
     if r < 0:
         raise PagedAttentionError("pa_decode_partition_tokens", r)
     return r
 
 
 def workspace_for(q, k_cache, block_tables, partition_tokens=0):
-    """A torch byte buffer of the size the decode calls need (None if none)."""
+    """A torch byte buffer of the size the decode call for k_cache's dtype needs
+    (None if none)."""
     import torch
 
     n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
-                                  block_tables.shape[1], k_cache.shape[2], partition_tokens)
+                                  block_tables.shape[1], k_cache.shape[2], partition_tokens,
+                                  k_cache.dtype == torch.int8)
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 

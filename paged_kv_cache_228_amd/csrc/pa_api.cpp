@@ -22,10 +22,14 @@ int hip_fail(hipError_t e)
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Partition size in blocks. An explicit request is honoured up to the
-// 256-block staging limit. Otherwise the largest of 32, 16, 8, 4 blocks
-// (512 .. 64 tokens) that still gives at least 2048 workgroups for the
-// longest possible context, so the 256 compute units each get several.
-int choose_part_blocks(int num_seqs, int num_kv_heads, int max_blocks, int partition_tokens)
+// 256-block staging limit. Otherwise the largest of a dtype-dependent start
+// (fp16: 128 blocks = 2048 tokens, INT8: 64 blocks = 1024 tokens) and its
+// halvings down to 4 blocks that still gives at least 2048 workgroups for the
+// longest possible context, so every compute unit gets several. Long
+// partitions amortise each workgroup's set-up and the merge; INT8 tiles cost
+// more arithmetic per byte, so its waves stream better in shorter runs.
+int choose_part_blocks(int num_seqs, int num_kv_heads, int max_blocks, int partition_tokens,
+                       bool int8)
 {
     int pb;
     if (partition_tokens > 0) {
@@ -33,7 +37,7 @@ int choose_part_blocks(int num_seqs, int num_kv_heads, int max_blocks, int parti
     } else {
         pb = 4;
         const long long units = (long long)num_seqs * num_kv_heads;
-        for (int cand : {32, 16, 8}) {
+        for (int cand = int8 ? 64 : 128; cand > 4; cand >>= 1) {
             const long long parts = (max_blocks + cand - 1) / cand;
             if (units * parts >= 2048) {
                 pb = cand;
@@ -82,7 +86,7 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
 
-    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens);
+    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens, int8);
     const int parts = (max_blocks_per_seq + pb - 1) / pb;
     if (parts > 1) {
         const size_t need = pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
@@ -163,23 +167,26 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
 }
 
 int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
-                               int block_size, int partition_tokens)
+                               int block_size, int partition_tokens, int kv_int8)
 {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
         partition_tokens < 0 || partition_tokens % pa::kBlockTokens)
         return PA_ERR_SHAPE;
     if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
-    return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens) *
+    return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens,
+                              kv_int8 != 0) *
            pa::kBlockTokens;
 }
 
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                                 int max_blocks_per_seq, int block_size, int partition_tokens)
+                                 int max_blocks_per_seq, int block_size, int partition_tokens,
+                                 int kv_int8)
 {
     if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_blocks_per_seq, 1, partition_tokens))
         return 0;
-    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens);
+    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens,
+                                      kv_int8 != 0);
     const int parts = (max_blocks_per_seq + pb - 1) / pb;
     if (parts <= 1) return 0;
     return pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);

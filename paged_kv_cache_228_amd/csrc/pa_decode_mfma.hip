@@ -9,22 +9,28 @@
 // h, out = sum_t softmax_t(scale * q.k_t) v_t over the sequence's tokens.
 //
 // Work decomposition: one wave (the whole workgroup) per (sequence, KV head,
-// context partition). The wave stages the partition's block ids in LDS and
-// streams the partition's (block, head) tiles through a ring of register
-// buffers, so several tiles' loads are in flight while one is computed.
+// context partition). The wave stages the partition's block ids (and, for
+// INT8, the tiles' scales) in LDS and streams the partition's (block, head)
+// tiles in slots of SLOT consecutive blocks through a two-slot register ring:
+// one slot's loads are in flight while the other slot is computed.
 //
-// Per 16-token tile, with the G <= 16 query heads of the KV head padded to
-// the 16 columns of a 16x16 MFMA tile:
-//   S^T[token][head] = K[token][:] . Q^T[:][head]     v_mfma_f32_16x16x32_f16
-//   O[head][dim]    += P[head][token] . V[token][dim]  v_mfma_f32_16x16x16_f16
-// The lane map of the first product's result (lane = head + 16 * g holds
-// tokens 4g .. 4g+3) is exactly the lane map the second product wants for
-// its P operand, so scores never move between lanes. P goes to the matrix
-// core as two fp16 halves (hi + lo, about 20 significant bits); K and V enter
+// Per 16-token tile, with the G <= 8 query heads of the KV head in the 16
+// columns of the MFMA tile:
+//   S^T[token][col] = K[token][:] . Q^T[:][col]        v_mfma_f32_16x16x32_f16
+// and per pair of tiles (32 tokens)
+//   O[row][dim]    += P[row][token] . V[token][dim]    v_mfma_f32_16x16x32_f16
+// The lane map of the first product's result (lane = column + 16 * g holds
+// tokens 4g .. 4g+3) is the lane map the second product wants for its P
+// operand (lane = row + 16 * g holds k = 8g .. 8g+7, here tokens 4g .. 4g+3
+// of the pair's first tile, then of its second), so scores never move between
+// lanes. Columns 0..7 of Q^T hold the group's heads and columns 8..15 the
+// same heads again, so rows h and h + 8 of P carry the fp16 hi and lo halves
+// of head h's weights (about 20 significant bits together) and one product
+// covers both; the two output rows are added once at the end. K and V enter
 // as fp16 (INT8 codes convert to fp16 exactly). Accumulation is fp32.
 //
 // Online softmax with a lazy reference: scores are kept in the log2 domain;
-// the running reference max m of each head is only raised when a tile holds a
+// the running reference max m of each head is only raised when a slot holds a
 // score more than kLazy above it, so p = 2^(s - m) <= 2^kLazy and the rescale
 // of the accumulators is rare. The result is the same softmax: every partial
 // sum carries the same reference, and the merge divides it out.
@@ -34,7 +40,6 @@ namespace pa {
 namespace {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -45,20 +50,39 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer descriptor, 32-
 constexpr float kLazy = 8.0f;                 // log2 headroom before the reference max moves
 constexpr float kPScale = 64.0f;              // P enters the matrix core as p * 2^6 (<= 2^14)
 constexpr float kPUnscale = 1.0f / 64.0f;
-#ifndef PA_KV_AUX
-#define PA_KV_AUX 0
-#endif
+
 // Grid order: the KV heads of one (sequence, partition) are neighbours in
 // dispatch order, so the head tiles of each physical block (adjacent in the
 // pool) are read at about the same time.
 #ifndef PA_HEAD_FAST
 #define PA_HEAD_FAST 1
 #endif
-#ifndef PA_WG_HEADS
-#define PA_WG_HEADS 0
+// Blocks per ring slot (even): a slot's tiles are loaded together and
+// computed together; two slots form the ring.
+#ifndef PA_SLOT_F16
+#define PA_SLOT_F16 4
 #endif
-constexpr int kKvAux = PA_KV_AUX;  // cache-policy bits of the K/V tile loads
+#ifndef PA_SLOT_I8
+#define PA_SLOT_I8 2
+#endif
+// Cache-policy bits of the K/V tile loads (2: non-temporal).
+#ifndef PA_KV_AUX
+#define PA_KV_AUX 2
+#endif
+// Waves per SIMD the register allocation must leave room for. A ring of two
+// 4-tile fp16 slots needs more than half of the register file, so fp16 runs
+// one wave per SIMD with 32 KiB of loads in flight per wave; INT8 tiles are
+// half the size and run two.
+#ifndef PA_MINW_F16
+#define PA_MINW_F16 1
+#endif
+#ifndef PA_MINW_I8
+#define PA_MINW_I8 2
+#endif
 
+// Element i of a 4-dword vector (i a compile-time constant after unrolling).
+// Written as a select chain: subscripting an array of ext-vector values with
+// a loop index inside nested unrolled loops lost elements with this compiler.
 __device__ __forceinline__ uint32_t word(const u32x4& v, int i)
 {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -74,7 +98,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes)
 }
 
 // Sum / max over the four lanes that share l % 16 (lanes l, l^16, l^32, l^48).
-// Outside the per-tile fast path only, so the LDS-routed shuffle is cheap
+// Outside the per-slot fast path only, so the LDS-routed shuffle is cheap
 // enough. (The permlane16/32 swap builtins were tried here; with both
 // operands the same value this compiler folded the pair of results into one.)
 __device__ __forceinline__ float sum_over_groups(float x)
@@ -106,19 +130,19 @@ __device__ __forceinline__ void codes_to_h2(uint32_t w, h2_t& lo, h2_t& hi)
     hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
 }
 
-// Byte b of code words w0 and w1 (already sign-flipped) as an exact fp16 pair.
-__device__ __forceinline__ h2_t code_pair(uint32_t u0, uint32_t u1, int b)
+// Byte b of sign-flipped code words u0 and u1 as an exact fp16 pair.
+__device__ __forceinline__ uint32_t code_pair(uint32_t u0, uint32_t u1, int b)
 {
     const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
     const uint32_t two = __builtin_amdgcn_perm(u1, u0, sel) | 0x64006400u;
     const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    return __builtin_bit_cast(h2_t, two) - bias;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, two) - bias);
 }
 
 // Half h (0/1) of fp16 words w0 and w1 as a pair.
-__device__ __forceinline__ h2_t half_pair(uint32_t w0, uint32_t w1, int h)
+__device__ __forceinline__ uint32_t half_pair(uint32_t w0, uint32_t w1, int h)
 {
-    return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u));
+    return __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u);
 }
 
 template <int D, bool I8>
@@ -126,7 +150,7 @@ struct MCfg {
     static constexpr int EB = I8 ? 1 : 2;      // bytes per element
     static constexpr int ROW = D * EB;         // bytes per token row of a tile
     static constexpr int TILE = 16 * ROW;      // bytes per (block, head) tile
-    static constexpr int NQK = D / 32;         // 16x16x32 MFMAs for Q.K^T
+    static constexpr int NQK = D / 32;         // 16x16x32 MFMAs for Q.K^T per tile
     static constexpr int KLD = I8 ? (NQK + 1) / 2 : NQK;  // 16-byte K loads per lane
     static constexpr int DPL = D / 16;         // V dims per lane
     static constexpr int VB = DPL * EB;        // V bytes per lane per token
@@ -140,9 +164,9 @@ template <> struct VChunk<4> { typedef uint32_t type; };
 template <int VB>
 __device__ __forceinline__ typename VChunk<VB>::type vload(rsrc_t r, int off)
 {
-    if constexpr (VB == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kKvAux);
-    else if constexpr (VB == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kKvAux);
-    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kKvAux);
+    if constexpr (VB == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_KV_AUX);
+    else if constexpr (VB == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PA_KV_AUX);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, PA_KV_AUX);
 }
 
 template <int D, bool I8>
@@ -150,15 +174,14 @@ struct MTile {
     using C = MCfg<D, I8>;
     u32x4 k[C::KLD];
     typename VChunk<C::VB>::type v[4];
-    float ksc, vsc;  // INT8 scales of the (block, head); unused for fp16
 };
 
 // Issue every load of one tile. valid == false (past the partition) or an id
 // outside the pool gives a zero-byte descriptor: the loads return zeros and
 // touch no memory.
 template <int D, bool I8>
-__device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, rsrc_t scales_k,
-                                      rsrc_t scales_v, int bid, bool valid, int kvh, int lane)
+__device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, int bid, bool valid,
+                                      int kvh, int lane)
 {
     using C = MCfg<D, I8>;
     const bool in_pool = valid && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks;
@@ -168,141 +191,248 @@ __device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, rsrc
     const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
     const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + off, bytes);
     const int g = lane >> 4, n = lane & 15;
+    // K in the tile's own order: instruction c reads bytes [1024c, 1024c + 1024)
 #pragma unroll
-    for (int c = 0; c < C::KLD; ++c) {
-        // fp16: chunk 4c+g of token n (dims 8(4c+g) ..); int8: chunk g+4c (dims 16(g+4c) ..)
-        const int chunk = I8 ? (g + 4 * c) : (4 * c + g);
-        t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, n * C::ROW + 16 * chunk, 0, kKvAux);
-    }
+    for (int c = 0; c < C::KLD; ++c) t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * c + 16 * lane, 0, PA_KV_AUX);
+    // V: token 4g+ks, this lane's DPL dims (n * DPL ..)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) t.v[ks] = vload<C::VB>(rv, (4 * g + ks) * C::ROW + n * C::VB);
-    if constexpr (I8) {
-        const int si = (int)(b * a.num_kv_heads + kvh) * 4;
-        t.ksc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scales_k, in_pool ? si : -4, 0, 0));
-        t.vsc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(scales_v, in_pool ? si : -4, 0, 0));
+}
+
+// K reaches the matrix cores through LDS. A load in operand order (lane =
+// token) would make each 64-lane load instruction touch sixteen 128-byte lines
+// and use half of each, which costs the vector memory path about twice the
+// time of reading the same bytes in order; so K is read in order (eight whole
+// lines per instruction), written to a per-wave LDS tile and read back in
+// operand order. The 16-byte chunk q of row r sits at chunk q ^ f(r), an XOR
+// swizzle for which both the in-order writes and the operand-order reads hit
+// distinct LDS banks (whether the hardware serves 8 lanes per 128 bytes or
+// 16 lanes per 256 bytes per pass).
+template <int D, bool I8>
+struct KSwz {
+    using C = MCfg<D, I8>;
+    static_assert(C::ROW == 256 || C::ROW == 128 || C::ROW == 64, "row of 64, 128 or 256 bytes");
+    static constexpr int KREG = C::TILE / 1024;  // 16-byte registers per lane per tile
+    __device__ static int f(int r)
+    {
+        if constexpr (C::ROW == 256) return r & 15;
+        else if constexpr (C::ROW == 128) return ((r >> 1) & 3) | (((r ^ (r >> 3)) & 1) << 2);
+        else return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
     }
+    // index (in 16-byte units) of chunk q of row r in an LDS tile
+    __device__ static int at(int r, int q) { return r * (C::ROW / 16) + (q ^ f(r)); }
+};
+
+// Rearrange the K registers of one tile from tile order to operand order
+// through the wave's LDS tile `kl`: afterwards k[c] holds, for lane (g, n),
+// token n's 16-byte chunk 4c+g (fp16) or g+4c (INT8).
+template <int D, bool I8, int KL>
+__device__ __forceinline__ void k_to_operand(u32x4 (&k)[KL], u32x4* kl, int lane)
+{
+    using C = MCfg<D, I8>;
+    static_assert(KL == C::KLD, "K registers of one tile");
+    using S = KSwz<D, I8>;
+    static_assert(S::KREG == C::KLD, "one 16-byte register per 1024 bytes of K");
+    const int g = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) {
+        const int o = 1024 * c + 16 * lane;
+        kl[S::at(o / C::ROW, (o % C::ROW) / 16)] = k[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) k[c] = kl[S::at(n, I8 ? (g + 4 * c) : (4 * c + g))];
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int D, bool I8>
 struct MState {
     using C = MCfg<D, I8>;
-    f4_t acc[C::DPL];  // O[heads 4g..4g+3][dim DPL*n + nb] x 2^6
+    f4_t acc[C::DPL];  // rows 4g..4g+3 of O x 2^6 (row h: hi part of head h, row h+8: lo part)
     float m;           // reference max of head n (log2 domain)
     float l;           // this lane's share of head n's softmax denominator
 };
 
+// Scores of one tile, S^T = K . Q^T, times `sl` (softmax scale x log2 e, x
+// the tile's K scale for INT8).
 template <int D, bool I8>
-__device__ __forceinline__ void mprocess(MState<D, I8>& st, MTile<D, I8>& t,
-                                         const h8_t (&qb)[MCfg<D, I8>::NQK], int valid,
-                                         float scale_log2, int lane)
+__device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, I8>::KLD],
+                                            const h8_t (&qb)[MCfg<D, I8>::NQK], float sl)
 {
     using C = MCfg<D, I8>;
-    const int g = lane >> 4;
-
-    // S^T = K . Q^T
     f4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < C::NQK; ++c) {
         h8_t ka;
         if constexpr (I8) {
-            const u32x4& w = t.k[c >> 1];
+            const u32x4& w = kop[c >> 1];
             h2_t p0, p1, p2, p3;
             codes_to_h2(word(w, 2 * (c & 1)), p0, p1);
             codes_to_h2(word(w, 2 * (c & 1) + 1), p2, p3);
             ka = h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
         } else {
-            ka = __builtin_bit_cast(h8_t, t.k[c]);
+            ka = __builtin_bit_cast(h8_t, kop[c]);
         }
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], s, 0, 0, 0);
     }
-    const float sl = I8 ? scale_log2 * t.ksc : scale_log2;
-    float sc[4];
+    return s * sl;
+}
+
+// The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
+template <int D, bool I8>
+__device__ __forceinline__ uint32_t v_word(const MTile<D, I8>& t, int nb, int h)
+{
+    if constexpr (I8) {
+        return code_pair(word(t.v[2 * h], nb >> 2) ^ 0x80808080u,
+                         word(t.v[2 * h + 1], nb >> 2) ^ 0x80808080u, nb & 3);
+    } else {
+        return half_pair(word(t.v[2 * h], nb >> 1), word(t.v[2 * h + 1], nb >> 1), nb & 1);
+    }
+}
+
+// One slot: SLOT consecutive tiles of the partition, of which the first
+// `valid0` token rows are live (every row when valid0 >= 16 * SLOT, none when
+// valid0 <= 0).
+template <int D, bool I8, int SLOT>
+__device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (&t)[SLOT],
+                                         const h8_t (&qb)[MCfg<D, I8>::NQK], int valid0,
+                                         float scale_log2, const float (&ksc)[SLOT],
+                                         const float (&vsc)[SLOT], int lane, bool lo_row,
+                                         u32x4* kl)
+{
+    using C = MCfg<D, I8>;
+    const int g = lane >> 4;
+    float sc[SLOT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = s[i] * sl;
-    if (valid < 16) {  // tail of the sequence: mask scores and zero the V rows
+    for (int u = 0; u < SLOT; ++u) {
+        u32x4 kop[C::KLD];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * g + i >= valid) {
-                sc[i] = -INFINITY;
-                if constexpr (C::VB == 16) t.v[i] = u32x4{0u, 0u, 0u, 0u};
-                else if constexpr (C::VB == 8) t.v[i] = u32x2{0u, 0u};
-                else t.v[i] = 0u;
-            }
+        for (int c = 0; c < C::KLD; ++c) kop[c] = t[u].k[c];
+        k_to_operand<D, I8, C::KLD>(kop, kl + u * (C::TILE / 16), lane);
+        const f4_t s = tile_scores<D, I8>(kop, qb, I8 ? scale_log2 * ksc[u] : scale_log2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[u][i] = s[i];
+    }
+    // dead rows (past the sequence's end or the partition's) get score -inf
+    // and a zero V row (their stored slots may hold anything, NaN included);
+    // V rows are masked where the P.V operands are built, so the tile
+    // registers themselves are only ever read
+    uint32_t vmask[SLOT][2];
+#pragma unroll
+    for (int u = 0; u < SLOT; ++u) vmask[u][0] = vmask[u][1] = 0xFFFFFFFFu;
+    if (valid0 < 16 * SLOT) {
+#pragma unroll
+        for (int u = 0; u < SLOT; ++u) {
+            const int vu = valid0 - 16 * u;  // live rows of tile u (may be <= 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * g + i >= vu) sc[u][i] = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                vmask[u][h] = (4 * g + 2 * h < vu ? 0x0000FFFFu : 0u) |
+                              (4 * g + 2 * h + 1 < vu ? 0xFFFF0000u : 0u);
+        }
     }
 
-    // lazy online softmax
-    const float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    // lazy online softmax over the whole slot
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < SLOT; ++u)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
     if (__builtin_amdgcn_ballot_w64(mx > st.m + kLazy) != 0) {
         const float mn = fmaxf(st.m, max_over_groups(mx));
-        const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // 0 on the first tile
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mn);  // 0 on the first slot
         st.l *= alpha;
         st.m = mn;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float ai = from_lane(alpha, 4 * g + i);  // alpha of head 4g+i
+            const float ai = from_lane(alpha, 4 * g + i);  // alpha of row 4g+i's head
 #pragma unroll
             for (int nb = 0; nb < C::DPL; ++nb) st.acc[nb][i] *= ai;
         }
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(sc[i] - st.m);
-        st.l += p[i];
-    }
-    // P x 2^6 (<= 2^14) as fp16 hi + lo
-    float ps[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] = p[i] * kPScale;
-    const h2_t hi01 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[0], ps[1]));
-    const h2_t hi23 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[2], ps[3]));
-    const h2_t lo01 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(
-                                                   ps[0] - (float)hi01.x, ps[1] - (float)hi01.y));
-    const h2_t lo23 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(
-                                                   ps[2] - (float)hi23.x, ps[3] - (float)hi23.y));
-    const h4_t pa_hi = {hi01.x, hi01.y, hi23.x, hi23.y};
-    const h4_t pa_lo = {lo01.x, lo01.y, lo23.x, lo23.y};
 
-    // O += P . V, one 16x16x16 product per dim slot nb of the lane
+    // INT8: each tile's weights are scaled by its V scale relative to the
+    // slot's largest (<= 1, so P keeps its fp16 range); the slot's product
+    // then enters the running sum times that largest scale
+    float vref = 1.0f;
+    float vrel[SLOT];
+#pragma unroll
+    for (int u = 0; u < SLOT; ++u) vrel[u] = 1.0f;
     if constexpr (I8) {
-        uint32_t u[4][C::VB / 4];
+        vref = vsc[0];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+        for (int u = 1; u < SLOT; ++u) vref = fmaxf(vref, vsc[u]);
+        const float inv = vref > 0.0f ? 1.0f / vref : 0.0f;
 #pragma unroll
-            for (int w = 0; w < C::VB / 4; ++w) u[ks][w] = word(t.v[ks], w) ^ 0x80808080u;
+        for (int u = 0; u < SLOT; ++u) vrel[u] = vsc[u] * inv;
+    }
+
+    f4_t tacc[C::DPL];
+    if constexpr (I8) {
+#pragma unroll
+        for (int nb = 0; nb < C::DPL; ++nb) tacc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int pr = 0; pr < SLOT / 2; ++pr) {
+        // P of the pair (x 2^6 <= 2^14, x the tile's relative V scale): the
+        // hi half in rows 0..7, the lo half in rows 8..15
+        uint32_t pw[4];
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+            const int u = 2 * pr + uu;
+            float ps[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(sc[u][i] - st.m);
+                st.l += p;
+                ps[i] = p * (kPScale * vrel[u]);
+            }
+            const h2_t hi01 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[0], ps[1]));
+            const h2_t hi23 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[2], ps[3]));
+            if (lo_row) {
+                pw[2 * uu] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_pkrtz(ps[0] - (float)hi01.x, ps[1] - (float)hi01.y));
+                pw[2 * uu + 1] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_pkrtz(ps[2] - (float)hi23.x, ps[3] - (float)hi23.y));
+            } else {
+                pw[2 * uu] = __builtin_bit_cast(uint32_t, hi01);
+                pw[2 * uu + 1] = __builtin_bit_cast(uint32_t, hi23);
+            }
+        }
+        const h8_t pa = __builtin_bit_cast(h8_t, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        const MTile<D, I8>& ta = t[2 * pr];
+        const MTile<D, I8>& tb = t[2 * pr + 1];
 #pragma unroll
         for (int nb = 0; nb < C::DPL; ++nb) {
-            const h2_t b01 = code_pair(u[0][nb >> 2], u[1][nb >> 2], nb & 3);
-            const h2_t b23 = code_pair(u[2][nb >> 2], u[3][nb >> 2], nb & 3);
-            const h4_t vb = {b01.x, b01.y, b23.x, b23.y};
-            // the tile's own product in fresh accumulators, then scaled by
-            // the tile's V scale into the running sum (P never carries vsc,
-            // so its fp16 range does not depend on the data's scale)
-            f4_t tacc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_hi, vb, f4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            tacc = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_lo, vb, tacc, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.acc[nb][i] = __builtin_fmaf(t.vsc, tacc[i], st.acc[nb][i]);
+            const u32x4 vw = {v_word<D, I8>(ta, nb, 0) & vmask[2 * pr][0],
+                              v_word<D, I8>(ta, nb, 1) & vmask[2 * pr][1],
+                              v_word<D, I8>(tb, nb, 0) & vmask[2 * pr + 1][0],
+                              v_word<D, I8>(tb, nb, 1) & vmask[2 * pr + 1][1]};
+            const h8_t vb = __builtin_bit_cast(h8_t, vw);
+            if constexpr (I8)
+                tacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, tacc[nb], 0, 0, 0);
+            else
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, st.acc[nb], 0, 0, 0);
         }
-    } else {
+    }
+    if constexpr (I8) {
 #pragma unroll
-        for (int nb = 0; nb < C::DPL; ++nb) {
-            const h2_t b01 = half_pair(word(t.v[0], nb >> 1), word(t.v[1], nb >> 1), nb & 1);
-            const h2_t b23 = half_pair(word(t.v[2], nb >> 1), word(t.v[3], nb >> 1), nb & 1);
-            const h4_t vb = {b01.x, b01.y, b23.x, b23.y};
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_hi, vb, st.acc[nb], 0, 0, 0);
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa_lo, vb, st.acc[nb], 0, 0, 0);
-        }
+        for (int nb = 0; nb < C::DPL; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.acc[nb][i] = __builtin_fmaf(vref, tacc[nb][i], st.acc[nb][i]);
     }
 }
 
-template <int D, bool I8, int NBUF>
-__global__ __launch_bounds__(PA_WG_HEADS ? 512 : 64) void decode_mfma_kernel(DecodeArgs a, int group)
+template <int D, bool I8, int SLOT, int MINW>
+__global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int group)
 {
+    static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     using C = MCfg<D, I8>;
-    const int p = PA_WG_HEADS ? blockIdx.x : (PA_HEAD_FAST ? blockIdx.y : blockIdx.x);
-    const int kvh = PA_WG_HEADS ? uniform(threadIdx.x >> 6) : (PA_HEAD_FAST ? blockIdx.x : blockIdx.y);
-    const int s = PA_WG_HEADS ? blockIdx.y : blockIdx.z;
-    const int lane = threadIdx.x & 63;
+    const int p = PA_HEAD_FAST ? blockIdx.y : blockIdx.x;
+    const int kvh = PA_HEAD_FAST ? blockIdx.x : blockIdx.y;
+    const int s = blockIdx.z;
+    const int lane = threadIdx.x;
     const int g = lane >> 4, n = lane & 15;
     const int hq0 = kvh * group;
 
@@ -318,20 +448,38 @@ __global__ __launch_bounds__(PA_WG_HEADS ? 512 : 64) void decode_mfma_kernel(Dec
     if (b0 >= nblk) return;
     const int nloc = min(nblk - b0, a.part_blocks);
     const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
+    // token rows of the partition, counted from its first block
+    const int live = min(ctx, (b0 + nloc) * kBlockTokens) - b0 * kBlockTokens;
 
-    __shared__ int ids[kMaxPartitionBlocks];
-    for (int i = PA_WG_HEADS ? (int)threadIdx.x : lane; i < nloc; i += PA_WG_HEADS ? (int)blockDim.x : 64)
-        ids[i] = a.tables[(int64_t)s * a.max_blocks + b0 + i];
+    // the partition's block ids (and, for INT8, the two scales of each
+    // block's tile) staged in LDS: one entry per block, read back as a
+    // broadcast per tile
+    __shared__ int4 meta[kMaxPartitionBlocks];
+    __shared__ u32x4 kl[SLOT * C::TILE / 16];  // K of one slot on its way to operand order
+    for (int i = lane; i < nloc; i += 64) {
+        const int bid = a.tables[(int64_t)s * a.max_blocks + b0 + i];
+        float ksc = 0.0f, vsc = 0.0f;
+        if (I8 && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks) {
+            const int64_t si = (int64_t)bid * a.num_kv_heads + kvh;
+            ksc = a.k_scale[si];
+            vsc = a.v_scale[si];
+        }
+        meta[i] = int4{bid, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
+    }
 
-    // Q^T as the B operand of the 16x16x32 products: lane (g, n) holds head n,
-    // the same 8 dims its K chunk covers; heads past the group are zero.
+    // Q^T as the B operand of the 16x16x32 products: lane (g, n) holds head
+    // n mod 8 (columns 8..15 repeat the group so that rows 8..15 of P can
+    // carry the lo halves), the same 8 dims its K chunk covers; heads past
+    // the group are zero.
+    const int qh = n & 7;
+    const bool lo_row = n >= 8;
     h8_t qb[C::NQK];
     {
-        const _Float16* qrow = static_cast<const _Float16*>(a.q) + ((int64_t)s * a.num_q_heads + hq0 + n) * D;
+        const _Float16* qrow = static_cast<const _Float16*>(a.q) + ((int64_t)s * a.num_q_heads + hq0 + qh) * D;
 #pragma unroll
         for (int c = 0; c < C::NQK; ++c) {
             const int d0 = I8 ? 16 * (g + 4 * (c >> 1)) + 8 * (c & 1) : 8 * (4 * c + g);
-            if (n < group)
+            if (qh < group)
                 qb[c] = __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + d0));
             else
                 qb[c] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -342,39 +490,53 @@ __global__ __launch_bounds__(PA_WG_HEADS ? 512 : 64) void decode_mfma_kernel(Dec
     for (int nb = 0; nb < C::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
     st.m = -INFINITY;
     st.l = 0.0f;
-
-    const rsrc_t rks = make_rsrc(a.k_scale, I8 ? (int)min<int64_t>(a.num_blocks * a.num_kv_heads * 4, 0x7fffffff) : 0);
-    const rsrc_t rvs = make_rsrc(a.v_scale, I8 ? (int)min<int64_t>(a.num_blocks * a.num_kv_heads * 4, 0x7fffffff) : 0);
     __syncthreads();
 
-    // ring of NBUF tiles: tile j sits in buf[j % NBUF]; tile j + NBUF - 1 is
-    // loaded while tile j is processed
-    MTile<D, I8> buf[NBUF];
+    // Two-slot ring: one slot is computed while the other's loads are in
+    // flight. Tiles past the partition load nothing (zero-byte descriptors)
+    // and all their rows are dead; the loop has no early exit, so the last
+    // step may compute one empty slot.
+    MTile<D, I8> ring[2][SLOT];
+    float ks[2][SLOT], vs[2][SLOT];
+    auto load_slot = [&](int r, int j0) {
 #pragma unroll
-    for (int b = 0; b < NBUF - 1; ++b)
-        mload<D, I8>(buf[b], a, rks, rvs, uniform(ids[b < nloc ? b : 0]), b < nloc, kvh, lane);
-    for (int base = 0; base < nloc; base += NBUF) {
-#pragma unroll
-        for (int b = 0; b < NBUF; ++b) {
-            const int j = base + b;
-            if (j >= nloc) break;
-            const int jn = j + NBUF - 1;
-            mload<D, I8>(buf[(b + NBUF - 1) % NBUF], a, rks, rvs, uniform(ids[jn < nloc ? jn : 0]),
-                         jn < nloc, kvh, lane);
-            const int valid = ctx - (b0 + j) * kBlockTokens;
-            mprocess<D, I8>(st, buf[b], qb, valid, a.scale_log2, lane);
+        for (int u = 0; u < SLOT; ++u) {
+            const int j = j0 + u;
+            const int4 e = meta[j < nloc ? j : 0];
+            mload<D, I8>(ring[r][u], a, uniform(e.x), j < nloc, kvh, lane);
+            ks[r][u] = __builtin_bit_cast(float, uniform(e.y));
+            vs[r][u] = __builtin_bit_cast(float, uniform(e.z));
         }
+    };
+    load_slot(0, 0);
+    for (int j = 0; j < nloc; j += 2 * SLOT) {
+        load_slot(1, j + SLOT);
+        __builtin_amdgcn_sched_barrier(0);
+        mprocess<D, I8, SLOT>(st, ring[0], qb, live - j * kBlockTokens, a.scale_log2, ks[0], vs[0],
+                              lane, lo_row, kl);
+        __builtin_amdgcn_sched_barrier(0);
+        load_slot(0, j + 2 * SLOT);
+        __builtin_amdgcn_sched_barrier(0);
+        mprocess<D, I8, SLOT>(st, ring[1], qb, live - (j + SLOT) * kBlockTokens, a.scale_log2,
+                              ks[1], vs[1], lane, lo_row, kl);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // epilogue: the denominator of head n, summed over the four lane groups
+    // epilogue: fold the lo rows (8..15, lane groups 2 and 3) onto the hi rows
+    // (0..7, lane groups 0 and 1); the denominator of head n, summed over the
+    // four lane groups
+#pragma unroll
+    for (int nb = 0; nb < C::DPL; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32, 64);
     const float lsum = sum_over_groups(st.l);
     const int64_t row0 = (int64_t)s * a.num_q_heads + hq0;
     if (nparts == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int hd = 4 * g + i;
-            const float inv = kPUnscale / from_lane(lsum, hd & 15);
-            if (hd < group) {
+            const int hd = 4 * g + i;  // rows of lane groups 0 and 1 only
+            const float inv = kPUnscale / from_lane(lsum, hd & 7);
+            if (g < 2 && hd < group) {
                 float* o = a.out + (row0 + hd) * D + n * C::DPL;
 #pragma unroll
                 for (int nb = 0; nb < C::DPL; ++nb) o[nb] = st.acc[nb][i] * inv;
@@ -385,7 +547,7 @@ __global__ __launch_bounds__(PA_WG_HEADS ? 512 : 64) void decode_mfma_kernel(Dec
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hd = 4 * g + i;
-            if (hd < group) {
+            if (g < 2 && hd < group) {
                 float* o = a.ws + ((row0 + hd) * a.max_parts + p) * D + n * C::DPL;
 #pragma unroll
                 for (int nb = 0; nb < C::DPL; ++nb) o[nb] = st.acc[nb][i] * kPUnscale;
@@ -401,27 +563,18 @@ __global__ __launch_bounds__(PA_WG_HEADS ? 512 : 64) void decode_mfma_kernel(Dec
 
 }  // namespace
 
-// Ring depths: tiles of one wave in flight (loads) plus the one being computed.
-#ifndef PA_RING_F16
-#define PA_RING_F16 2
-#endif
-#ifndef PA_RING_I8
-#define PA_RING_I8 3
-#endif
-
 hipError_t launch_decode_partitions_mfma(const DecodeArgs& a, int head_dim, int group, bool int8,
                                          hipStream_t st)
 {
-    const dim3 grid = PA_WG_HEADS ? dim3(a.max_parts, a.num_seqs)
-                      : (PA_HEAD_FAST ? dim3(a.num_kv_heads, a.max_parts, a.num_seqs)
-                                      : dim3(a.max_parts, a.num_kv_heads, a.num_seqs));
-    const dim3 block(PA_WG_HEADS ? 64 * a.num_kv_heads : 64);
+    const dim3 grid = PA_HEAD_FAST ? dim3(a.num_kv_heads, a.max_parts, a.num_seqs)
+                                   : dim3(a.max_parts, a.num_kv_heads, a.num_seqs);
+    const dim3 block(64);
     if (head_dim == 128) {
-        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<128, true, PA_RING_I8>), grid, block, 0, st, a, group);
-        else hipLaunchKernelGGL((decode_mfma_kernel<128, false, PA_RING_F16>), grid, block, 0, st, a, group);
+        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<128, true, PA_SLOT_I8, PA_MINW_I8>), grid, block, 0, st, a, group);
+        else hipLaunchKernelGGL((decode_mfma_kernel<128, false, PA_SLOT_F16, PA_MINW_F16>), grid, block, 0, st, a, group);
     } else if (head_dim == 64) {
-        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<64, true, PA_RING_I8>), grid, block, 0, st, a, group);
-        else hipLaunchKernelGGL((decode_mfma_kernel<64, false, PA_RING_F16>), grid, block, 0, st, a, group);
+        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<64, true, PA_SLOT_I8, PA_MINW_I8>), grid, block, 0, st, a, group);
+        else hipLaunchKernelGGL((decode_mfma_kernel<64, false, PA_SLOT_F16, PA_MINW_F16>), grid, block, 0, st, a, group);
     } else {
         return hipErrorInvalidValue;
     }

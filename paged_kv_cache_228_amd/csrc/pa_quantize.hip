@@ -10,6 +10,17 @@
 //             x / scale an IEEE fp32 division; scale 0 gives code 0.
 // One wave per tile: 16-byte loads (1 KiB of contiguous bytes per wave
 // instruction), wave-wide max, then 8-byte stores of packed codes.
+//
+// The quotient x / scale is formed without a full division per element: with
+// r = 1 / scale correctly rounded (one IEEE division per tile),
+//     q0 = RN(x r),  e = x - q0 scale (exact, one fma),  q = RN(q0 + e r)
+// is the correctly rounded quotient (Markstein's correction step; Handbook of
+// Floating-Point Arithmetic, Muller et al., section on division with fma).
+// For this kernel's domain that was also checked exhaustively: every fp16 x
+// with |x| <= amax, for every finite fp16 amax > 0, gives RN(x / scale) bit
+// for bit. rint and the int8 conversion use the 1.5 * 2^23 shift: adding it
+// rounds a value below 2^22 in magnitude to the nearest integer (ties to
+// even) and leaves that integer, two's complement, in the low mantissa bits.
 #include "pa_internal.h"
 
 namespace pa {
@@ -45,11 +56,31 @@ __device__ __forceinline__ float wave_max(float x)
     return x;
 }
 
-__device__ __forceinline__ uint32_t code_of(float x, float scale)
+// Non-temporal loads and stores: the fp16 tiles are read once and the codes
+// are read by a later kernel; without the hint the written lines linger in
+// the caches in a state that slowed the next reader of those addresses by
+// about a fifth.
+#ifndef PA_Q_NT
+#define PA_Q_NT 1
+#endif
+
+// Low byte of the 1.5 * 2^23-shifted code of x (see the file comment).
+__device__ __forceinline__ uint32_t shifted_code(float x, float scale, float r)
 {
-    float r = rintf(x / scale);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)(int32_t)r & 0xFFu;
+    const float q0 = __fmul_rn(x, r);
+    const float e = __builtin_fmaf(-q0, scale, x);
+    const float q = __builtin_fmaf(e, r, q0);
+    const float c = __builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
+    return __builtin_bit_cast(uint32_t, __fadd_rn(c, 12582912.0f));
+}
+
+// Codes of the four fp16 values in words w0, w1, packed as four bytes.
+__device__ __forceinline__ uint32_t pack4(uint32_t w0, uint32_t w1, float scale, float r)
+{
+    const h2_t a = __builtin_bit_cast(h2_t, w0), b = __builtin_bit_cast(h2_t, w1);
+    const uint32_t t0 = shifted_code((float)a.x, scale, r), t1 = shifted_code((float)a.y, scale, r);
+    const uint32_t t2 = shifted_code((float)b.x, scale, r), t3 = shifted_code((float)b.y, scale, r);
+    return __builtin_amdgcn_perm(t1, t0, 0x0C0C0400u) | __builtin_amdgcn_perm(t3, t2, 0x04000C0Cu);
 }
 
 template <int D>
@@ -68,38 +99,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
     if (b < 0 || b >= a.num_blocks) return;
 
     const int64_t tile = (b * a.num_kv_heads + h) * (int64_t)(kBlockTokens * D);
-    const uint16_t* src = (tensor ? a.v : a.k) + tile;
-    int8_t* dst = (tensor ? a.vc : a.kc) + tile;
+    const u32x4* src = reinterpret_cast<const u32x4*>((tensor ? a.v : a.k) + tile);
+    u32x2* dst = reinterpret_cast<u32x2*>((tensor ? a.vc : a.kc) + tile);
     float* sdst = (tensor ? a.vs : a.ks) + b * a.num_kv_heads + h;
 
     u32x4 x[kChunks];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) x[c] = reinterpret_cast<const u32x4*>(src)[lane + 64 * c];
+    for (int c = 0; c < kChunks; ++c)
+        x[c] = PA_Q_NT ? __builtin_nontemporal_load(src + lane + 64 * c) : src[lane + 64 * c];
 
-    float amax = 0.0f;
+    // max |x| on fp16 pairs (clearing the sign bits is an exact fabs)
+    h2_t m2 = {(_Float16)0.0f, (_Float16)0.0f};
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const h2_t v = __builtin_bit_cast(h2_t, word(x[c], w));
-            amax = fmaxf(amax, fmaxf(fabsf((float)v.x), fabsf((float)v.y)));
-        }
-    amax = wave_max(amax);
+        for (int w = 0; w < 4; ++w)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(h2_t, word(x[c], w) & 0x7FFF7FFFu));
+    const float amax = wave_max(fmaxf((float)m2.x, (float)m2.y));
     const float scale = amax / 127.0f;
     if (lane == 0) *sdst = scale;
+    const float rcp = 1.0f / scale;  // correctly rounded; unused when scale is 0
 
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-        uint32_t packed[2] = {0u, 0u};
+        u32x2 packed = {0u, 0u};
         if (scale != 0.0f) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const h2_t v = __builtin_bit_cast(h2_t, word(x[c], w));
-                const uint32_t two = code_of((float)v.x, scale) | (code_of((float)v.y, scale) << 8);
-                packed[w >> 1] |= two << (16 * (w & 1));
-            }
+            packed.x = pack4(word(x[c], 0), word(x[c], 1), scale, rcp);
+            packed.y = pack4(word(x[c], 2), word(x[c], 3), scale, rcp);
         }
-        reinterpret_cast<u32x2*>(dst)[lane + 64 * c] = u32x2{packed[0], packed[1]};
+        if (PA_Q_NT)
+            __builtin_nontemporal_store(packed, dst + lane + 64 * c);
+        else
+            dst[lane + 64 * c] = packed;
     }
 }
 

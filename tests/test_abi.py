@@ -112,9 +112,15 @@ def test_workspace_and_partition_sizing():
     assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5) == 2 * 4 * 2 * 66 * 4
     # one partition covers the whole context: no workspace
     assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5, 16, 80) == 0
-    # 64 seqs x 8 KV heads, up to 1024 blocks: 512-token partitions, 32 of them
-    assert pa.pa_decode_partition_tokens(64, 8, 1024) == 512
-    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024) == 64 * 32 * 32 * 130 * 4
+    # 64 seqs x 8 KV heads, up to 1024 blocks: fp16 takes 2048-token partitions
+    # (8 of them), INT8 1024-token ones (16)
+    assert pa.pa_decode_partition_tokens(64, 8, 1024) == 2048
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024) == 64 * 32 * 8 * 130 * 4
+    assert pa.pa_decode_partition_tokens(64, 8, 1024, kv_int8=True) == 1024
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_int8=True) == 64 * 32 * 16 * 130 * 4
+    # fewer (sequence, KV head) pairs: shorter partitions keep >= 2048 workgroups
+    assert pa.pa_decode_partition_tokens(8, 8, 1024) == 512
+    assert pa.pa_decode_partition_tokens(8, 8, 1024, kv_int8=True) == 512
     # explicit sizes are honoured up to 4096 tokens per partition
     assert pa.pa_decode_partition_tokens(1, 1, 1024, 16, 16) == 16
     assert pa.pa_decode_partition_tokens(1, 1, 1024, 16, 1 << 20) == 4096
