@@ -31,6 +31,25 @@ METRIC = "decode attn tokens/sec + achieved HBM GB/s (% of peak), fp16 & INT8 KV
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 
 
+def measured_traffic(call: str, workload: str):
+    """HBM bytes per launch of `call` from the committed counter profile, or None
+    when there is none for this workload or the kernel sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get("calls", {}).get(call)
+    if rec is None:
+        return None
+    for src, digest in rec["sources"].items():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,6 +61,9 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and output check)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many bytes "
+                         "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path is "
@@ -56,6 +78,13 @@ def main() -> int:
 
     pa.lib()  # fail loudly before any work if the library is missing
     dev = torch.device("cuda:0")
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_gen = time.time()
     w = {
         "mixed_prefix": W.mixed_prefix,
@@ -135,8 +164,11 @@ def main() -> int:
     call = {"quantize": "pa_quantize_kv_int8", "fp16": "pa_paged_decode_f16",
             "int8": "pa_paged_decode_int8"}
     roofline = {"bound": "hbm", "achieved": paths[dom]["gbs"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": paths[dom]["frac_of_peak"], "traffic": None,
-                "kernel": call[dom]}
+                "unit": "GB/s", "frac": paths[dom]["frac_of_peak"],
+                "traffic": measured_traffic(call[dom], w.name), "kernel": call[dom]}
+    if roofline["traffic"] is not None:
+        roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"
+        roofline["traffic_over_alg"] = round(roofline["traffic"] / alg[dom], 4)
 
     result = {
         "metric": METRIC,

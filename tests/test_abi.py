@@ -129,3 +129,24 @@ def test_workspace_and_partition_sizing():
     assert pa.pa_decode_workspace_bytes(1, 3, 2, 64, 8) == 0
     with pytest.raises(pa.PagedAttentionError):
         pa.pa_decode_partition_tokens(1, 1, 8, 16, 20)
+
+
+def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
+    import hashlib
+    import json
+
+    import bench
+
+    (tmp_path / "profiles").mkdir()
+    src = tmp_path / "k.hip"
+    src.write_text("kernel v1\n")
+    rec = {"calls": {"pa_paged_decode_f16": {
+        "fetch_bytes": 1000, "write_bytes": 24,
+        "sources": {"k.hip": hashlib.sha256(b"kernel v1\n").hexdigest()}}}}
+    (tmp_path / "profiles" / "hbm_traffic_wl.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("pa_paged_decode_f16", "wl") == 1024
+    assert bench.measured_traffic("pa_paged_decode_int8", "wl") is None
+    assert bench.measured_traffic("pa_paged_decode_f16", "other") is None
+    src.write_text("kernel v2\n")
+    assert bench.measured_traffic("pa_paged_decode_f16", "wl") is None
