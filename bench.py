@@ -110,9 +110,9 @@ def main() -> int:
     out8 = torch.empty_like(out16)
     ws16 = pa.workspace_for(q, k16, tables, args.partition_tokens)
     ws8 = pa.workspace_for(q, k8, tables, args.partition_tokens)
-    part = {name: pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_blocks_per_seq,
-                                                16, args.partition_tokens, kv_int8=i8)
-            for name, i8 in (("fp16", False), ("int8", True))}
+    shares = {name: pa.pa_decode_shares(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
+                                        16, args.partition_tokens, kv_int8=i8)
+              for name, i8 in (("fp16", False), ("int8", True))}
     torch.cuda.synchronize()
 
     def step(ev):
@@ -188,7 +188,7 @@ def main() -> int:
             "ctx_min": int(w.context_lens.min()), "ctx_max": int(w.context_lens.max()),
             "num_q_heads": w.num_q_heads, "num_kv_heads": hkv, "head_dim": d,
             "block_size": 16, "pool_blocks": w.num_blocks, "live_blocks": n_live,
-            "partition_tokens": part,
+            "shares_per_kv_head": shares,
             "step": "quantize live blocks + fp16 decode + int8 decode",
         },
         "paths": paths,

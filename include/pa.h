@@ -26,7 +26,7 @@
  *    groups; paged-attention-runtime summary item 4, GQA expanded).
  *  - q: fp16 [num_seqs][num_q_heads][head_dim]; out: fp32, same shape.
  *    block_tables: int32 [num_seqs][max_blocks_per_seq]; context_lens: int32
- *    [num_seqs]. q, pools, codes and out must be 16-byte aligned.
+ *    [num_seqs]. q, pools, codes, out and workspace must be 16-byte aligned.
  *  - Errors found on the host (NULL pointers, bad shapes, unsupported sizes,
  *    a workspace that is too small) return a negative code before anything
  *    is launched. A launch failure returns PA_ERR_HIP; pa_error_string then
@@ -51,7 +51,7 @@ enum {
     PA_ERR_NULL = -1,        /* a required pointer is NULL */
     PA_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
     PA_ERR_UNSUPPORTED = -3, /* valid but not built: block_size, head_dim, group size, alignment */
-    PA_ERR_WORKSPACE = -4,   /* split-K workspace missing or smaller than required */
+    PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
     PA_ERR_HIP = -5          /* a HIP call failed; see pa_error_string */
 };
 
@@ -80,22 +80,27 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
                         int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
                         int head_dim, void* stream);
 
-/* Bytes of split-K workspace a decode call with these sizes needs (0 when the
- * context fits one partition). partition_tokens: tokens per context partition,
- * a multiple of 16, or 0 to let the library choose; partitions are capped at
- * 4096 tokens. kv_int8: 0 for pa_paged_decode_f16, nonzero for
- * pa_paged_decode_int8 (the automatic partition size depends on the KV
- * dtype). Returns 0 for arguments the decode calls would reject. */
+/* Work split of the decode calls. For every KV head the tiles of all
+ * sequences, in sequence order, are cut into equal contiguous shares, one
+ * 64-lane wave each; a (sequence, KV head) whose tiles fall in one share is
+ * finished by that wave, one cut by share boundaries is completed by a merge
+ * kernel from the shares' partial results (log-sum-exp combine).
+ * partition_tokens: the wanted tokens per share for the longest possible
+ * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
+ * to let the library size one share per wave the current device holds at
+ * once. kv_int8: 0 for pa_paged_decode_f16, nonzero for pa_paged_decode_int8.
+ *
+ * pa_decode_shares returns the number of shares per KV head, or a negative
+ * PA_ERR_* code for arguments the decode calls would reject.
+ * pa_decode_workspace_bytes returns the workspace a decode call with these
+ * arguments needs (tile prefix sums and partials; always more than 0), or 0
+ * for arguments the decode calls would reject. Both depend on the current
+ * device's compute-unit count when partition_tokens is 0. */
+int pa_decode_shares(int num_seqs, int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                     int block_size, int partition_tokens, int kv_int8);
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_blocks_per_seq, int block_size, int partition_tokens,
                                  int kv_int8);
-
-/* Tokens per context partition the decode call for this KV dtype (kv_int8 as
- * above) will use for these sizes (the library's choice when
- * partition_tokens is 0), or a negative PA_ERR_* code for arguments the
- * decode calls would reject. */
-int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
-                               int block_size, int partition_tokens, int kv_int8);
 
 /* Decode attention over an fp16 paged KV cache. For every sequence s and
  * query head h, with n = context_lens[s] and k_t, v_t the K/V rows of token t
@@ -103,10 +108,12 @@ int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_pe
  *     out[s][h] = sum_t softmax_t(softmax_scale * q[s][h] . k_t) * v_t
  * computed with a single-pass online softmax in fp32 (paged-attention-runtime
  * summary, "CORE CAPABILITIES" 2; glossary monograph section 5.2,
- * softmax(Q K^T / sqrt(d))). Long contexts are split into partitions whose
- * partial results are merged by a second, stream-ordered kernel; workspace
- * must then hold pa_decode_workspace_bytes(...) bytes (it may be NULL when
- * that is 0). num_seqs may be 0 (nothing is launched). */
+ * softmax(Q K^T / sqrt(d))). Three stream-ordered kernels: the work split
+ * (prefix sums of the context lengths), the decode waves and the merge (see
+ * pa_decode_shares). workspace: at least pa_decode_workspace_bytes(...) bytes
+ * of device memory owned by the caller, overwritten by every call; calls that
+ * share a workspace must not overlap. num_seqs may be 0 (nothing is
+ * launched, workspace may be NULL). */
 int pa_paged_decode_f16(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens, float* out,
                         int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

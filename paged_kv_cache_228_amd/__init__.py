@@ -36,7 +36,7 @@ EXPORTED = (
     "pa_error_string",
     "pa_quantize_kv_int8",
     "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens",
+    "pa_decode_shares",
     "pa_paged_decode_f16",
     "pa_paged_decode_int8",
 )
@@ -66,8 +66,8 @@ def lib() -> C.CDLL:
         L.pa_quantize_kv_int8.restype = i32
         L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_workspace_bytes.restype = sz
-        L.pa_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32]
-        L.pa_decode_partition_tokens.restype = i32
+        L.pa_decode_shares.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.pa_decode_shares.restype = i32
         tail = [p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, i32, p, sz, p]
         L.pa_paged_decode_f16.argtypes = [p, p, p] + tail
         L.pa_paged_decode_f16.restype = i32
@@ -131,12 +131,12 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max
                                                int(bool(kv_int8))))
 
 
-def pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq, block_size=16,
-                               partition_tokens=0, kv_int8=False) -> int:
-    r = int(lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq,
-                                             block_size, partition_tokens, int(bool(kv_int8))))
+def pa_decode_shares(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, block_size=16,
+                     partition_tokens=0, kv_int8=False) -> int:
+    r = int(lib().pa_decode_shares(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                   block_size, partition_tokens, int(bool(kv_int8))))
     if r < 0:
-        raise PagedAttentionError("pa_decode_partition_tokens", r)
+        raise PagedAttentionError("pa_decode_shares", r)
     return r
 
 
@@ -211,6 +211,6 @@ def pa_paged_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables, co
 
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
-    "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_partition_tokens",
+    "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8",
 ]

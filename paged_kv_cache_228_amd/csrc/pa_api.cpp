@@ -3,6 +3,7 @@
 // call are in include/pa.h.
 #include "pa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -21,34 +22,36 @@ int hip_fail(hipError_t e)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Partition size in blocks. An explicit request is honoured up to the
-// 256-block staging limit. Otherwise the largest of a dtype-dependent start
-// (fp16: 128 blocks = 2048 tokens, INT8: 64 blocks = 1024 tokens) and its
-// halvings down to 4 blocks that still gives at least 2048 workgroups for the
-// longest possible context, so every compute unit gets several. Long
-// partitions amortise each workgroup's set-up and the merge; INT8 tiles cost
-// more arithmetic per byte, so its waves stream better in shorter runs.
-int choose_part_blocks(int num_seqs, int num_kv_heads, int max_blocks, int partition_tokens,
-                       bool int8)
+// Compute units of the current device (256 when there is none to ask).
+int num_compute_units()
 {
-    int pb;
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        return v;
+    return 256;
+}
+
+// Shares per KV head (see pa_internal.h). An explicit partition_tokens asks
+// for shares of about that many tokens, sized for the longest possible batch
+// (num_seqs x max_blocks_per_seq blocks). Otherwise one wave per share fills
+// the device once: compute units x decode waves per unit, split over the KV
+// heads, and no share shorter than 8 blocks of that bound. Never more shares
+// than the bound has blocks.
+long long shares_per_head(int num_seqs, int num_kv_heads, int head_dim, int max_blocks,
+                          int partition_tokens, bool int8)
+{
+    const long long bound = (long long)num_seqs * max_blocks;
+    if (bound <= 0) return 1;
+    long long k;
     if (partition_tokens > 0) {
-        pb = partition_tokens / pa::kBlockTokens;
+        k = (bound * pa::kBlockTokens + partition_tokens - 1) / partition_tokens;
     } else {
-        pb = 4;
-        const long long units = (long long)num_seqs * num_kv_heads;
-        for (int cand = int8 ? 64 : 128; cand > 4; cand >>= 1) {
-            const long long parts = (max_blocks + cand - 1) / cand;
-            if (units * parts >= 2048) {
-                pb = cand;
-                break;
-            }
-        }
+        const long long waves = (long long)num_compute_units() * pa::decode_waves_per_cu(head_dim, int8);
+        k = std::max(1LL, waves / num_kv_heads);
+        k = std::min(k, (bound + 7) / 8);
     }
-    if (pb > pa::kMaxPartitionBlocks) pb = pa::kMaxPartitionBlocks;
-    if (pb > max_blocks) pb = max_blocks;
-    if (pb < 1) pb = 1;
-    return pb;
+    return std::max(1LL, std::min(k, bound));
 }
 
 int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -66,6 +69,13 @@ int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head
     if (group < 1 || group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
     if ((long long)max_blocks_per_seq * pa::kBlockTokens > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    // tile prefix sums are int32; one workgroup per (share, KV head)
+    if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    if (shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, false) *
+                num_kv_heads > 0x7fffffffLL ||
+        shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, true) *
+                num_kv_heads > 0x7fffffffLL)
+        return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -86,13 +96,11 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
 
-    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens, int8);
-    const int parts = (max_blocks_per_seq + pb - 1) / pb;
-    if (parts > 1) {
-        const size_t need = pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
-        if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-    }
-    if (parts > 65535) return PA_ERR_UNSUPPORTED;  // one grid dimension per partition index
+    const int shares = (int)shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                            partition_tokens, int8);
+    const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, head_dim, shares);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
 
     pa::DecodeArgs a;
     a.q = q;
@@ -103,14 +111,15 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     a.tables = tables;
     a.ctx = ctx;
     a.out = out;
-    a.ws = static_cast<float*>(workspace);
+    a.rows = static_cast<int32_t*>(workspace);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      pa::workspace_int_bytes(num_seqs, shares));
     a.num_blocks = num_blocks;
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.max_blocks = max_blocks_per_seq;
-    a.part_blocks = pb;
-    a.max_parts = parts;
+    a.shares = shares;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, int8,
                                      static_cast<hipStream_t>(stream));
@@ -166,16 +175,18 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
-int pa_decode_partition_tokens(int num_seqs, int num_kv_heads, int max_blocks_per_seq,
-                               int block_size, int partition_tokens, int kv_int8)
+int pa_decode_shares(int num_seqs, int num_kv_heads, int head_dim, int max_blocks_per_seq,
+                     int block_size, int partition_tokens, int kv_int8)
 {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
         partition_tokens < 0 || partition_tokens % pa::kBlockTokens)
         return PA_ERR_SHAPE;
     if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
-    return choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens,
-                              kv_int8 != 0) *
-           pa::kBlockTokens;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    return (int)std::min(shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                         partition_tokens, kv_int8 != 0),
+                         0x7fffffffLL);
 }
 
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -185,11 +196,9 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
     if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_blocks_per_seq, 1, partition_tokens))
         return 0;
-    const int pb = choose_part_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, partition_tokens,
-                                      kv_int8 != 0);
-    const int parts = (max_blocks_per_seq + pb - 1) / pb;
-    if (parts <= 1) return 0;
-    return pa::workspace_floats(num_seqs, num_q_heads, parts, head_dim) * sizeof(float);
+    const long long shares = shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                             partition_tokens, kv_int8 != 0);
+    return pa::workspace_bytes(num_seqs, num_q_heads, head_dim, (int)shares);
 }
 
 int pa_paged_decode_f16(const void* q, const void* k_cache, const void* v_cache,

@@ -35,6 +35,7 @@
 // of the accumulators is rare. The result is the same softmax: every partial
 // sum carries the same reference, and the merge divides it out.
 #include "pa_internal.h"
+#include "pa_split.h"
 
 namespace pa {
 namespace {
@@ -44,19 +45,14 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer descriptor, 32-bit format
 constexpr float kLazy = 8.0f;                 // log2 headroom before the reference max moves
-constexpr float kPScale = 64.0f;              // P enters the matrix core as p * 2^6 (<= 2^14)
+constexpr float kPScale = 64.0f;              // P enters the matrix core as p * 2^6 (<= 2^14, INT8 <= 2^15)
 constexpr float kPUnscale = 1.0f / 64.0f;
 
-// Grid order: the KV heads of one (sequence, partition) are neighbours in
-// dispatch order, so the head tiles of each physical block (adjacent in the
-// pool) are read at about the same time.
-#ifndef PA_HEAD_FAST
-#define PA_HEAD_FAST 1
-#endif
 // Blocks per ring slot (even): a slot's tiles are loaded together and
 // computed together; two slots form the ring.
 #ifndef PA_SLOT_F16
@@ -119,18 +115,9 @@ __device__ __forceinline__ float from_lane(float x, int src)
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-// Four signed INT8 codes (one dword) to two pairs of exact fp16 values:
-// flipping the sign bit gives c + 128; under the fp16 pattern 0x64xx that
-// byte reads 1024 + c + 128, and subtracting 1152 leaves c.
-__device__ __forceinline__ void codes_to_h2(uint32_t w, h2_t& lo, h2_t& hi)
-{
-    const uint32_t u = w ^ 0x80808080u;
-    const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    lo = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;
-    hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
-}
-
-// Byte b of sign-flipped code words u0 and u1 as an exact fp16 pair.
+// Byte b of sign-flipped code words u0 and u1 as an exact fp16 pair. Flipping
+// the sign bit of a code c gives the byte c + 128; under the fp16 pattern
+// 0x64xx that byte reads 1024 + c + 128, and subtracting 1152 leaves c.
 __device__ __forceinline__ uint32_t code_pair(uint32_t u0, uint32_t u1, int b)
 {
     const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
@@ -251,31 +238,111 @@ struct MState {
     f4_t acc[C::DPL];  // rows 4g..4g+3 of O x 2^6 (row h: hi part of head h, row h+8: lo part)
     float m;           // reference max of head n (log2 domain)
     float l;           // this lane's share of head n's softmax denominator
+    float vr;          // INT8: reference V scale of acc (uniform; 0 until a nonzero scale)
 };
 
-// Scores of one tile, S^T = K . Q^T, times `sl` (softmax scale x log2 e, x
-// the tile's K scale for INT8).
+// The query operand of S^T = K . Q^T (B operand; lane (g, n) serves column n,
+// i.e. head n mod 8, over the same dims as its K chunk).
+//  fp16 K: q as fp16, 8 dims per 16x16x32 product.
+//  INT8 K: the codes go to v_mfma_i32_16x16x64_i8 unconverted, so q is split
+//  per head into three int8 parts with a power-of-two step sigma
+//  (max |q| / sigma in [32, 64)): q = sigma (a1 + a2 2^-7 + a3 2^-14) + r,
+//  |r| <= sigma 2^-15, so every q element of at least max |q| / 1024 is exact
+//  and the rest are off by less than 2^-20 max |q|. The three integer dot
+//  products are exact; they are recombined in fp32.
 template <int D, bool I8>
-__device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, I8>::KLD],
-                                            const h8_t (&qb)[MCfg<D, I8>::NQK], float sl)
+struct QOp;
+template <int D>
+struct QOp<D, false> {
+    h8_t b[MCfg<D, false>::NQK];
+};
+template <int D>
+struct QOp<D, true> {
+    u32x4 part[3][MCfg<D, true>::KLD];  // a1, a2, a3: 16 int8 per register
+    float sigma;                        // this lane's head's step
+};
+
+// Scores of one tile, S^T = K . Q^T (K registers in operand order), times
+// `sl` (softmax scale x log2 e, x the tile's K scale for INT8).
+template <int D, bool I8>
+__device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, I8>::KLD], const QOp<D, I8>& qo,
+                                            float sl)
 {
     using C = MCfg<D, I8>;
-    f4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (I8) {
+        i32x4 s1 = {0, 0, 0, 0}, s2 = {0, 0, 0, 0}, s3 = {0, 0, 0, 0};
 #pragma unroll
-    for (int c = 0; c < C::NQK; ++c) {
-        h8_t ka;
-        if constexpr (I8) {
-            const u32x4& w = kop[c >> 1];
-            h2_t p0, p1, p2, p3;
-            codes_to_h2(word(w, 2 * (c & 1)), p0, p1);
-            codes_to_h2(word(w, 2 * (c & 1) + 1), p2, p3);
-            ka = h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-        } else {
-            ka = __builtin_bit_cast(h8_t, kop[c]);
+        for (int c = 0; c < C::KLD; ++c) {
+            const i32x4 k = __builtin_bit_cast(i32x4, kop[c]);
+            s1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k, __builtin_bit_cast(i32x4, qo.part[0][c]), s1, 0, 0, 0);
+            s2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k, __builtin_bit_cast(i32x4, qo.part[1][c]), s2, 0, 0, 0);
+            s3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(k, __builtin_bit_cast(i32x4, qo.part[2][c]), s3, 0, 0, 0);
         }
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], s, 0, 0, 0);
+        // |s1|, |s2|, |s3| <= 127 * 64 * D, so s2 * 2^7 + s3 stays in int32
+        const float f = sl * qo.sigma;
+        f4_t r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = __builtin_fmaf((float)(s2[i] * 128 + s3[i]), 1.0f / 16384.0f, (float)s1[i]) * f;
+        return r;
+    } else {
+        f4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < C::NQK; ++c)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kop[c]), qo.b[c], s, 0, 0, 0);
+        return s * sl;
     }
-    return s * sl;
+}
+
+// Build the query operand of lane (g, n) for head qh (zeros past the group).
+template <int D, bool I8>
+__device__ __forceinline__ void load_q(QOp<D, I8>& qo, const _Float16* qrow, bool live, int g)
+{
+    using C = MCfg<D, I8>;
+    if constexpr (I8) {
+        // dims 64c + 16g .. +15: the chunk g + 4c of this lane's K codes
+        float qf[C::KLD][16];
+        float mloc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C::KLD; ++c) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const h8_t v = live ? __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g + 8 * h))
+                                    : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    qf[c][8 * h + i] = (float)v[i];
+                    mloc = fmaxf(mloc, fabsf(qf[c][8 * h + i]));
+                }
+            }
+        }
+        const float mh = max_over_groups(mloc);  // the four lanes of column n hold all of head n's dims
+        const int e = mh > 0.0f ? __builtin_amdgcn_frexp_expf(mh) : 0;  // mh = f 2^e, f in [0.5, 1)
+        const float inv = __builtin_ldexpf(1.0f, 6 - e);
+        qo.sigma = __builtin_ldexpf(1.0f, e - 6);
+#pragma unroll
+        for (int c = 0; c < C::KLD; ++c) {
+            uint32_t w[3][4] = {};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float y = qf[c][i] * inv;  // |y| < 64, exact
+                const float a1 = __builtin_rintf(y);
+                const float r1 = (y - a1) * 128.0f;
+                const float a2 = __builtin_rintf(r1);
+                const float a3 = __builtin_rintf((r1 - a2) * 128.0f);
+                w[0][i >> 2] |= ((uint32_t)(int)a1 & 0xFFu) << (8 * (i & 3));
+                w[1][i >> 2] |= ((uint32_t)(int)a2 & 0xFFu) << (8 * (i & 3));
+                w[2][i >> 2] |= ((uint32_t)(int)a3 & 0xFFu) << (8 * (i & 3));
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) qo.part[j][c] = u32x4{w[j][0], w[j][1], w[j][2], w[j][3]};
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < C::NQK; ++c)
+            qo.b[c] = live ? __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * c + g)))
+                           : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
 }
 
 // The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
@@ -290,14 +357,13 @@ __device__ __forceinline__ uint32_t v_word(const MTile<D, I8>& t, int nb, int h)
     }
 }
 
-// One slot: SLOT consecutive tiles of the partition, of which the first
-// `valid0` token rows are live (every row when valid0 >= 16 * SLOT, none when
-// valid0 <= 0).
-template <int D, bool I8, int SLOT>
+// One slot: SLOT consecutive tiles of the partition. With TAIL, only the first
+// `valid0` token rows are live (none when valid0 <= 0); without, all are.
+template <int D, bool I8, int SLOT, bool TAIL>
 __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (&t)[SLOT],
-                                         const h8_t (&qb)[MCfg<D, I8>::NQK], int valid0,
+                                         const QOp<D, I8>& qo, int valid0,
                                          float scale_log2, const float (&ksc)[SLOT],
-                                         const float (&vsc)[SLOT], int lane, bool lo_row,
+                                         const float (&vsc)[SLOT], int lane, float lo_sel,
                                          u32x4* kl)
 {
     using C = MCfg<D, I8>;
@@ -309,7 +375,7 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
 #pragma unroll
         for (int c = 0; c < C::KLD; ++c) kop[c] = t[u].k[c];
         k_to_operand<D, I8, C::KLD>(kop, kl + u * (C::TILE / 16), lane);
-        const f4_t s = tile_scores<D, I8>(kop, qb, I8 ? scale_log2 * ksc[u] : scale_log2);
+        const f4_t s = tile_scores<D, I8>(kop, qo, I8 ? scale_log2 * ksc[u] : scale_log2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[u][i] = s[i];
     }
@@ -318,9 +384,7 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
     // V rows are masked where the P.V operands are built, so the tile
     // registers themselves are only ever read
     uint32_t vmask[SLOT][2];
-#pragma unroll
-    for (int u = 0; u < SLOT; ++u) vmask[u][0] = vmask[u][1] = 0xFFFFFFFFu;
-    if (valid0 < 16 * SLOT) {
+    if constexpr (TAIL) {
 #pragma unroll
         for (int u = 0; u < SLOT; ++u) {
             const int vu = valid0 - 16 * u;  // live rows of tile u (may be <= 0)
@@ -352,31 +416,35 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
         }
     }
 
-    // INT8: each tile's weights are scaled by its V scale relative to the
-    // slot's largest (<= 1, so P keeps its fp16 range); the slot's product
-    // then enters the running sum times that largest scale
-    float vref = 1.0f;
+    // INT8: a lazy reference V scale, like the reference max. Each tile's
+    // weights are multiplied by its V scale over the reference (<= 2, so P
+    // keeps its fp16 range) and the products accumulate at the reference
+    // scale; the reference only moves, rescaling the accumulators, when a
+    // tile's scale exceeds twice it (on the first nonzero scale, and rarely
+    // after).
     float vrel[SLOT];
 #pragma unroll
     for (int u = 0; u < SLOT; ++u) vrel[u] = 1.0f;
     if constexpr (I8) {
-        vref = vsc[0];
+        float vmax = vsc[0];
 #pragma unroll
-        for (int u = 1; u < SLOT; ++u) vref = fmaxf(vref, vsc[u]);
-        const float inv = vref > 0.0f ? 1.0f / vref : 0.0f;
+        for (int u = 1; u < SLOT; ++u) vmax = fmaxf(vmax, vsc[u]);
+        if (vmax > 2.0f * st.vr) {
+            const float f = st.vr / vmax;  // 0 while the reference is 0: acc is still 0
+#pragma unroll
+            for (int nb = 0; nb < C::DPL; ++nb) st.acc[nb] *= f;
+            st.vr = vmax;
+        }
+        const float inv = st.vr > 0.0f ? 1.0f / st.vr : 0.0f;
 #pragma unroll
         for (int u = 0; u < SLOT; ++u) vrel[u] = vsc[u] * inv;
     }
 
-    f4_t tacc[C::DPL];
-    if constexpr (I8) {
-#pragma unroll
-        for (int nb = 0; nb < C::DPL; ++nb) tacc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
 #pragma unroll
     for (int pr = 0; pr < SLOT / 2; ++pr) {
-        // P of the pair (x 2^6 <= 2^14, x the tile's relative V scale): the
-        // hi half in rows 0..7, the lo half in rows 8..15
+        // P of the pair (x 2^6, x the tile's relative V scale: <= 2^15): rows
+        // 0..7 (lo_sel 0) take its round-toward-zero fp16 value, rows 8..15
+        // (lo_sel 1) what that rounding dropped
         uint32_t pw[4];
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
@@ -388,16 +456,13 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
                 st.l += p;
                 ps[i] = p * (kPScale * vrel[u]);
             }
-            const h2_t hi01 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[0], ps[1]));
-            const h2_t hi23 = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(ps[2], ps[3]));
-            if (lo_row) {
-                pw[2 * uu] = __builtin_bit_cast(
-                    uint32_t, __builtin_amdgcn_cvt_pkrtz(ps[0] - (float)hi01.x, ps[1] - (float)hi01.y));
-                pw[2 * uu + 1] = __builtin_bit_cast(
-                    uint32_t, __builtin_amdgcn_cvt_pkrtz(ps[2] - (float)hi23.x, ps[3] - (float)hi23.y));
-            } else {
-                pw[2 * uu] = __builtin_bit_cast(uint32_t, hi01);
-                pw[2 * uu + 1] = __builtin_bit_cast(uint32_t, hi23);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float a = ps[2 * hh], b = ps[2 * hh + 1];
+                const h2_t hi = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+                pw[2 * uu + hh] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(-lo_sel, (float)hi.x, a),
+                                                         __builtin_fmaf(-lo_sel, (float)hi.y, b)));
             }
         }
         const h8_t pa = __builtin_bit_cast(h8_t, u32x4{pw[0], pw[1], pw[2], pw[3]});
@@ -405,180 +470,212 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
         const MTile<D, I8>& tb = t[2 * pr + 1];
 #pragma unroll
         for (int nb = 0; nb < C::DPL; ++nb) {
-            const u32x4 vw = {v_word<D, I8>(ta, nb, 0) & vmask[2 * pr][0],
-                              v_word<D, I8>(ta, nb, 1) & vmask[2 * pr][1],
-                              v_word<D, I8>(tb, nb, 0) & vmask[2 * pr + 1][0],
-                              v_word<D, I8>(tb, nb, 1) & vmask[2 * pr + 1][1]};
-            const h8_t vb = __builtin_bit_cast(h8_t, vw);
-            if constexpr (I8)
-                tacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, tacc[nb], 0, 0, 0);
-            else
-                st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, st.acc[nb], 0, 0, 0);
+            u32x4 vw = {v_word<D, I8>(ta, nb, 0), v_word<D, I8>(ta, nb, 1), v_word<D, I8>(tb, nb, 0),
+                        v_word<D, I8>(tb, nb, 1)};
+            if constexpr (TAIL)
+                vw &= u32x4{vmask[2 * pr][0], vmask[2 * pr][1], vmask[2 * pr + 1][0], vmask[2 * pr + 1][1]};
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(h8_t, vw), st.acc[nb],
+                                                                0, 0, 0);
         }
-    }
-    if constexpr (I8) {
-#pragma unroll
-        for (int nb = 0; nb < C::DPL; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.acc[nb][i] = __builtin_fmaf(vref, tacc[nb][i], st.acc[nb][i]);
     }
 }
 
-template <int D, bool I8, int SLOT, int MINW>
-__global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int group)
+// A slot, with the tail masking compiled in only where it can be needed.
+template <int D, bool I8, int SLOT>
+__device__ __forceinline__ void mslot(MState<D, I8>& st, const MTile<D, I8> (&t)[SLOT],
+                                      const QOp<D, I8>& qo, int valid0,
+                                      float scale_log2, const float (&ksc)[SLOT],
+                                      const float (&vsc)[SLOT], int lane, float lo_sel, u32x4* kl)
 {
-    static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
+    if (valid0 >= 16 * SLOT)
+        mprocess<D, I8, SLOT, false>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
+    else
+        mprocess<D, I8, SLOT, true>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
+}
+
+// The end of one (sequence, KV head) segment of a share. If the segment is
+// the row's whole context its query heads' outputs are written; otherwise its
+// partial (acc, m, l) goes to slot `slot` of the share (0: the share's first
+// row, 1: its last) for the merge kernel.
+template <int D, bool I8>
+__device__ __forceinline__ void emit(MState<D, I8>& st, const DecodeArgs& a, int s, int kvh, int group,
+                                     int share, bool cut, int slot, int lane)
+{
     using C = MCfg<D, I8>;
-    const int p = PA_HEAD_FAST ? blockIdx.y : blockIdx.x;
-    const int kvh = PA_HEAD_FAST ? blockIdx.x : blockIdx.y;
-    const int s = blockIdx.z;
-    const int lane = threadIdx.x;
     const int g = lane >> 4, n = lane & 15;
-    const int hq0 = kvh * group;
-
-    int ctx = a.ctx[s];
-    ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : ctx);
-    if (ctx == 0) {  // empty context: the first partition writes the zero rows
-        if (p == 0)
-            for (int e = lane; e < group * D; e += 64) a.out[((int64_t)s * a.num_q_heads + hq0) * D + e] = 0.0f;
-        return;
-    }
-    const int nblk = (ctx + kBlockTokens - 1) / kBlockTokens;
-    const int b0 = p * a.part_blocks;
-    if (b0 >= nblk) return;
-    const int nloc = min(nblk - b0, a.part_blocks);
-    const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-    // token rows of the partition, counted from its first block
-    const int live = min(ctx, (b0 + nloc) * kBlockTokens) - b0 * kBlockTokens;
-
-    // the partition's block ids (and, for INT8, the two scales of each
-    // block's tile) staged in LDS: one entry per block, read back as a
-    // broadcast per tile
-    __shared__ int4 meta[kMaxPartitionBlocks];
-    __shared__ u32x4 kl[SLOT * C::TILE / 16];  // K of one slot on its way to operand order
-    for (int i = lane; i < nloc; i += 64) {
-        const int bid = a.tables[(int64_t)s * a.max_blocks + b0 + i];
-        float ksc = 0.0f, vsc = 0.0f;
-        if (I8 && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks) {
-            const int64_t si = (int64_t)bid * a.num_kv_heads + kvh;
-            ksc = a.k_scale[si];
-            vsc = a.v_scale[si];
-        }
-        meta[i] = int4{bid, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
-    }
-
-    // Q^T as the B operand of the 16x16x32 products: lane (g, n) holds head
-    // n mod 8 (columns 8..15 repeat the group so that rows 8..15 of P can
-    // carry the lo halves), the same 8 dims its K chunk covers; heads past
-    // the group are zero.
-    const int qh = n & 7;
-    const bool lo_row = n >= 8;
-    h8_t qb[C::NQK];
-    {
-        const _Float16* qrow = static_cast<const _Float16*>(a.q) + ((int64_t)s * a.num_q_heads + hq0 + qh) * D;
-#pragma unroll
-        for (int c = 0; c < C::NQK; ++c) {
-            const int d0 = I8 ? 16 * (g + 4 * (c >> 1)) + 8 * (c & 1) : 8 * (4 * c + g);
-            if (qh < group)
-                qb[c] = __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + d0));
-            else
-                qb[c] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-    }
-    MState<D, I8> st;
-#pragma unroll
-    for (int nb = 0; nb < C::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    st.m = -INFINITY;
-    st.l = 0.0f;
-    __syncthreads();
-
-    // Two-slot ring: one slot is computed while the other's loads are in
-    // flight. Tiles past the partition load nothing (zero-byte descriptors)
-    // and all their rows are dead; the loop has no early exit, so the last
-    // step may compute one empty slot.
-    MTile<D, I8> ring[2][SLOT];
-    float ks[2][SLOT], vs[2][SLOT];
-    auto load_slot = [&](int r, int j0) {
-#pragma unroll
-        for (int u = 0; u < SLOT; ++u) {
-            const int j = j0 + u;
-            const int4 e = meta[j < nloc ? j : 0];
-            mload<D, I8>(ring[r][u], a, uniform(e.x), j < nloc, kvh, lane);
-            ks[r][u] = __builtin_bit_cast(float, uniform(e.y));
-            vs[r][u] = __builtin_bit_cast(float, uniform(e.z));
-        }
-    };
-    load_slot(0, 0);
-    for (int j = 0; j < nloc; j += 2 * SLOT) {
-        load_slot(1, j + SLOT);
-        __builtin_amdgcn_sched_barrier(0);
-        mprocess<D, I8, SLOT>(st, ring[0], qb, live - j * kBlockTokens, a.scale_log2, ks[0], vs[0],
-                              lane, lo_row, kl);
-        __builtin_amdgcn_sched_barrier(0);
-        load_slot(0, j + 2 * SLOT);
-        __builtin_amdgcn_sched_barrier(0);
-        mprocess<D, I8, SLOT>(st, ring[1], qb, live - (j + SLOT) * kBlockTokens, a.scale_log2,
-                              ks[1], vs[1], lane, lo_row, kl);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // epilogue: fold the lo rows (8..15, lane groups 2 and 3) onto the hi rows
-    // (0..7, lane groups 0 and 1); the denominator of head n, summed over the
-    // four lane groups
+    // fold the lo rows (8..15, lane groups 2 and 3) onto the hi rows (0..7,
+    // lane groups 0 and 1); the denominator of head n, summed over the four
+    // lane groups
 #pragma unroll
     for (int nb = 0; nb < C::DPL; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32, 64);
     const float lsum = sum_over_groups(st.l);
-    const int64_t row0 = (int64_t)s * a.num_q_heads + hq0;
-    if (nparts == 1) {
+    const float unscale = I8 ? kPUnscale * st.vr : kPUnscale;  // back to the data's scale
+    if (!cut) {
+        const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)kvh * group;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int hd = 4 * g + i;  // rows of lane groups 0 and 1 only
-            const float inv = kPUnscale / from_lane(lsum, hd & 7);
+            const float inv = unscale / from_lane(lsum, hd & 7);
             if (g < 2 && hd < group) {
                 float* o = a.out + (row0 + hd) * D + n * C::DPL;
 #pragma unroll
                 for (int nb = 0; nb < C::DPL; ++nb) o[nb] = st.acc[nb][i] * inv;
             }
         }
-    } else {
-        const int64_t nslots = (int64_t)a.num_seqs * a.num_q_heads * a.max_parts;
+        return;
+    }
+    const int64_t nslot = (int64_t)a.shares * a.num_kv_heads * 2 * group;  // (share, head, slot, q) entries
+    const int64_t base = (((int64_t)share * a.num_kv_heads + kvh) * 2 + slot) * group;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hd = 4 * g + i;
-            if (g < 2 && hd < group) {
-                float* o = a.ws + ((row0 + hd) * a.max_parts + p) * D + n * C::DPL;
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g + i;
+        if (g < 2 && hd < group) {
+            float* o = a.part + (base + hd) * D + n * C::DPL;
 #pragma unroll
-                for (int nb = 0; nb < C::DPL; ++nb) o[nb] = st.acc[nb][i] * kPUnscale;
-            }
-        }
-        if (g == 0 && n < group) {
-            const int64_t slot = (row0 + n) * a.max_parts + p;
-            a.ws[nslots * D + slot] = st.m;
-            a.ws[nslots * (D + 1) + slot] = lsum;
+            for (int nb = 0; nb < C::DPL; ++nb) o[nb] = st.acc[nb][i] * unscale;
         }
     }
+    if (g == 0 && n < group) {
+        a.part[nslot * D + base + n] = st.m;
+        a.part[nslot * (D + 1) + base + n] = lsum;
+    }
+}
+
+// One wave per (share, KV head): consecutive workgroups take consecutive KV
+// heads of one share, so the head tiles of each physical block (adjacent in
+// the pool) are read at about the same time, each head by the same compute
+// die throughout.
+template <int D, bool I8, int SLOT, int MINW>
+__global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int group)
+{
+    static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
+    const int kvh = blockIdx.x % a.num_kv_heads;
+    const int share = blockIdx.x / a.num_kv_heads;
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, n = lane & 15;
+    const int32_t* rows = a.rows;  // tile prefix sums [S + 1], then first rows of shares
+    const int64_t total = rows[a.num_seqs];
+    const int64_t p0 = (int64_t)share * total / a.shares;
+    const int64_t p1 = (int64_t)(share + 1) * total / a.shares;
+    if (p0 >= p1) return;
+
+    // block ids (and, for INT8, the two scales of each block's tile) of the
+    // current chunk, staged in LDS and read back as a broadcast per tile
+    __shared__ int4 meta[kMaxChunkBlocks];
+    __shared__ u32x4 kl[SLOT * MCfg<D, I8>::TILE / 16];  // K of one slot on its way to operand order
+    // lane (g, n) serves head n mod 8 of the group; columns 8..15 repeat the
+    // group so that rows 8..15 of P can carry the lo halves
+    const int qh = n & 7;
+    const float lo_sel = n >= 8 ? 1.0f : 0.0f;
+
+    int s = rows[a.num_seqs + 1 + share];  // the row holding tile p0
+    int64_t pos = p0;
+    int j = (int)(p0 - rows[s]);
+    while (true) {
+        const int nblk = rows[s + 1] - rows[s];
+        const int nseg = (int)min((int64_t)(nblk - j), p1 - pos);
+        int ctx = a.ctx[s];
+        ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : ctx);
+
+        QOp<D, I8> qo;
+        load_q<D, I8>(qo,
+                      static_cast<const _Float16*>(a.q) + ((int64_t)s * a.num_q_heads + kvh * group + qh) * D,
+                      qh < group, g);
+        MState<D, I8> st;
+#pragma unroll
+        for (int nb = 0; nb < MCfg<D, I8>::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        st.m = -INFINITY;
+        st.l = 0.0f;
+        st.vr = 0.0f;
+
+        for (int c0 = 0; c0 < nseg; c0 += kMaxChunkBlocks) {
+            const int jb = j + c0;  // first block of the chunk within the row
+            const int nloc = min(nseg - c0, kMaxChunkBlocks);
+            // live token rows of the chunk, counted from its first block
+            const int live = min(ctx, (jb + nloc) * kBlockTokens) - jb * kBlockTokens;
+            __syncthreads();  // the previous chunk is done with meta
+            for (int i = lane; i < nloc; i += 64) {
+                const int bid = a.tables[(int64_t)s * a.max_blocks + jb + i];
+                float ksc = 0.0f, vsc = 0.0f;
+                if (I8 && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks) {
+                    const int64_t si = (int64_t)bid * a.num_kv_heads + kvh;
+                    ksc = a.k_scale[si];
+                    vsc = a.v_scale[si];
+                }
+                meta[i] = int4{bid, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
+            }
+            __syncthreads();
+
+            // Two-slot ring: one slot is computed while the other's loads are
+            // in flight. Tiles past the chunk load nothing (zero-byte
+            // descriptors) and all their rows are dead; the loop has no early
+            // exit, so the last step may compute one empty slot.
+            MTile<D, I8> ring[2][SLOT];
+            float ks[2][SLOT], vs[2][SLOT];
+            auto load_slot = [&](int r, int j0) {
+#pragma unroll
+                for (int u = 0; u < SLOT; ++u) {
+                    const int jj = j0 + u;
+                    const int4 e = meta[jj < nloc ? jj : 0];
+                    mload<D, I8>(ring[r][u], a, uniform(e.x), jj < nloc, kvh, lane);
+                    ks[r][u] = __builtin_bit_cast(float, uniform(e.y));
+                    vs[r][u] = __builtin_bit_cast(float, uniform(e.z));
+                }
+            };
+            load_slot(0, 0);
+            for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
+                load_slot(1, jj + SLOT);
+                __builtin_amdgcn_sched_barrier(0);
+                mslot<D, I8, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0],
+                                   lane, lo_sel, kl);
+                __builtin_amdgcn_sched_barrier(0);
+                load_slot(0, jj + 2 * SLOT);
+                __builtin_amdgcn_sched_barrier(0);
+                mslot<D, I8, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2,
+                                   ks[1], vs[1], lane, lo_sel, kl);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        emit<D, I8>(st, a, s, kvh, group, share, j > 0 || j + nseg < nblk, pos == p0 ? 0 : 1, lane);
+        pos += nseg;
+        if (pos >= p1) break;
+        do {  // the next row with tiles (one exists: pos < p1 <= total)
+            ++s;
+        } while (rows[s + 1] == rows[s]);
+        j = 0;
+    }
+}
+
+template <int D, bool I8, int SLOT, int MINW>
+hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
+{
+    const int64_t waves = (int64_t)a.shares * a.num_kv_heads;
+    hipLaunchKernelGGL((decode_mfma_kernel<D, I8, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a,
+                       group);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_partitions_mfma(const DecodeArgs& a, int head_dim, int group, bool int8,
-                                         hipStream_t st)
+int decode_waves_per_cu(int, bool int8)
 {
-    const dim3 grid = PA_HEAD_FAST ? dim3(a.num_kv_heads, a.max_parts, a.num_seqs)
-                                   : dim3(a.max_parts, a.num_kv_heads, a.num_seqs);
-    const dim3 block(64);
-    if (head_dim == 128) {
-        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<128, true, PA_SLOT_I8, PA_MINW_I8>), grid, block, 0, st, a, group);
-        else hipLaunchKernelGGL((decode_mfma_kernel<128, false, PA_SLOT_F16, PA_MINW_F16>), grid, block, 0, st, a, group);
-    } else if (head_dim == 64) {
-        if (int8) hipLaunchKernelGGL((decode_mfma_kernel<64, true, PA_SLOT_I8, PA_MINW_I8>), grid, block, 0, st, a, group);
-        else hipLaunchKernelGGL((decode_mfma_kernel<64, false, PA_SLOT_F16, PA_MINW_F16>), grid, block, 0, st, a, group);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    // 4 SIMDs per compute unit x the waves per SIMD the register allocation
+    // is bounded to; only a sizing hint for the number of shares
+    return 4 * (int8 ? PA_MINW_I8 : PA_MINW_F16);
+}
+
+hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st)
+{
+    if (head_dim == 128)
+        return int8 ? launch_waves<128, true, PA_SLOT_I8, PA_MINW_I8>(a, group, st)
+                    : launch_waves<128, false, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+    if (head_dim == 64)
+        return int8 ? launch_waves<64, true, PA_SLOT_I8, PA_MINW_I8>(a, group, st)
+                    : launch_waves<64, false, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace pa

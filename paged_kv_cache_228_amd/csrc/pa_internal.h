@@ -8,11 +8,17 @@
 namespace pa {
 
 constexpr int kBlockTokens = 16;   // tokens per physical KV block
-constexpr int kWaves = 4;          // waves per decode workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxPartitionBlocks = kThreads;  // one staged block id per thread
+constexpr int kMaxChunkBlocks = 256;  // block ids a decode wave stages in LDS at a time
 constexpr int kMaxGroup = 8;       // query heads per KV head
+constexpr int kPrepThreads = 1024; // the prefix-sum kernel's one workgroup
 
+// Work decomposition of the decode: for every KV head, the tiles of all
+// sequences in order (sequence-major, block-minor; T = sum of blocks per
+// sequence) are cut into `shares` contiguous ranges of equal length
+// (share k: [k T / shares, (k + 1) T / shares)); one wave per (share, KV head).
+// A (sequence, KV head) row lying inside one share is finished by that wave;
+// a row cut by share boundaries leaves one partial per share, merged by a
+// second kernel.
 struct DecodeArgs {
     const void* q;          // fp16 [S][Hq][D]
     const void* k;          // fp16 or int8 pool [NB][Hkv][16][D]
@@ -22,30 +28,41 @@ struct DecodeArgs {
     const int32_t* tables;  // [S][max_blocks]
     const int32_t* ctx;     // [S]
     float* out;             // fp32 [S][Hq][D]
-    float* ws;              // split-K partials, see pa_api.cpp for the layout
+    int32_t* rows;          // workspace ints, layout below
+    float* part;            // workspace partials, layout below
     int64_t num_blocks;
     int num_seqs;
     int num_q_heads;
     int num_kv_heads;
     int max_blocks;         // table row length
-    int part_blocks;        // blocks per context partition (<= kMaxPartitionBlocks)
-    int max_parts;          // partitions of the longest possible context
+    int shares;             // shares per KV head
     float scale_log2;       // softmax_scale * log2(e)
 };
 
-// Workspace layout (floats): acc [S][Hq][P][D], then m [S][Hq][P], then l [S][Hq][P].
-inline size_t workspace_floats(int S, int Hq, int P, int D)
+// Workspace, int32 part: tile prefix sums rows[S + 1]; the first row of
+// each share [shares]; per sequence the first and the last share holding its
+// tiles ([S] each; equal when one share holds them all or the context is
+// empty); padded to 256 bytes. Then fp32 partials: acc [shares][Hkv][2][G][D],
+// then m and l, each [shares][Hkv][2][G]; slot 0 of a share holds its first
+// row if that row is cut, slot 1 its last.
+inline size_t workspace_int_bytes(int S, int shares)
 {
-    return (size_t)S * Hq * P * (size_t)(D + 2);
+    return ((size_t)(3 * (size_t)S + 1 + shares) * 4 + 255) & ~(size_t)255;
 }
+inline size_t workspace_bytes(int S, int Hq, int D, int shares)
+{
+    return workspace_int_bytes(S, shares) + (size_t)shares * 2 * Hq * (size_t)(D + 2) * 4;
+}
+// Offsets (in int32) of the arrays after rows[S + 1].
+__host__ __device__ inline int64_t ws_first_row(int S) { return (int64_t)S + 1; }
+__host__ __device__ inline int64_t ws_row_first_share(int S, int shares) { return (int64_t)S + 1 + shares; }
+__host__ __device__ inline int64_t ws_row_last_share(int S, int shares) { return (int64_t)2 * S + 1 + shares; }
 
-// Partition kernel + (when max_parts > 1) the split-K merge kernel.
+// Work split (prefix sums) -> decode waves -> merge of cut rows, all on `st`.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st);
-hipError_t launch_decode_partitions_mfma(const DecodeArgs& a, int head_dim, int group, bool int8,
-                                         hipStream_t st);
-hipError_t launch_decode_partitions_valu(const DecodeArgs& a, int head_dim, int group, bool int8,
-                                         hipStream_t st);
-hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st);
+// Decode waves each compute unit holds at once for this configuration.
+int decode_waves_per_cu(int head_dim, bool int8);
 
 struct QuantArgs {
     const uint16_t* k;

@@ -74,6 +74,8 @@ def decode_i8(**over):
         (dict(q=FAKE + 8), pa.PA_ERR_UNSUPPORTED),
         (dict(mb=64, part=16), pa.PA_ERR_WORKSPACE),
         (dict(mb=64, part=16, ws=FAKE, wsb=100), pa.PA_ERR_WORKSPACE),
+        (dict(), pa.PA_ERR_WORKSPACE),
+        (dict(ws=FAKE + 8, wsb=1 << 20), pa.PA_ERR_UNSUPPORTED),
         (dict(S=0), pa.PA_OK),
     ],
 )
@@ -106,29 +108,35 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 16, 64, None) == pa.PA_OK
 
 
-def test_workspace_and_partition_sizing():
-    # few (sequence, KV head) pairs: the smallest automatic partition (64 tokens)
-    assert pa.pa_decode_partition_tokens(2, 2, 5) == 64
-    assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5) == 2 * 4 * 2 * 66 * 4
-    # one partition covers the whole context: no workspace
-    assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5, 16, 80) == 0
-    # 64 seqs x 8 KV heads, up to 1024 blocks: fp16 takes 2048-token partitions
-    # (8 of them), INT8 1024-token ones (16)
-    assert pa.pa_decode_partition_tokens(64, 8, 1024) == 2048
-    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024) == 64 * 32 * 8 * 130 * 4
-    assert pa.pa_decode_partition_tokens(64, 8, 1024, kv_int8=True) == 1024
-    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_int8=True) == 64 * 32 * 16 * 130 * 4
-    # fewer (sequence, KV head) pairs: shorter partitions keep >= 2048 workgroups
-    assert pa.pa_decode_partition_tokens(8, 8, 1024) == 512
-    assert pa.pa_decode_partition_tokens(8, 8, 1024, kv_int8=True) == 512
-    # explicit sizes are honoured up to 4096 tokens per partition
-    assert pa.pa_decode_partition_tokens(1, 1, 1024, 16, 16) == 16
-    assert pa.pa_decode_partition_tokens(1, 1, 1024, 16, 1 << 20) == 4096
-    assert pa.pa_decode_workspace_bytes(1, 1, 1, 64, 1024, 16, 4096) == 1 * 1 * 4 * 66 * 4
+def test_workspace_and_share_sizing():
+    # Without a device to ask, the library sizes for 256 compute units.
+    # A tiny batch: at most one share per 8 blocks of the 2 x 5-block bound.
+    assert pa.pa_decode_shares(2, 2, 64, 5) == 2
+    # int32 prefix sums [S + 1], share first rows [K], first and last share
+    # of each sequence [S] x 2, padded to 256 B; then the partials:
+    # K x 2 slots x Hq x (D + 2) floats
+    def ints(S, K, hkv):
+        return ((3 * S + 1 + K) * 4 + 255) // 256 * 256
+
+    assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5) == ints(2, 2, 2) + 2 * 2 * 4 * 66 * 4
+    # the mixed batch's shape: one share per resident wave (256 CUs x 4 SIMDs x
+    # 1 fp16 / 2 INT8 waves per SIMD at head_dim 128) over 8 KV heads
+    assert pa.pa_decode_shares(64, 8, 128, 1024) == 128
+    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_int8=True) == 256
+    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024)
+            == ints(64, 128, 8) + 128 * 2 * 32 * 130 * 4)
+    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_int8=True)
+            == ints(64, 256, 8) + 256 * 2 * 32 * 130 * 4)
+    # explicit share length: 1 x 1024 blocks x 16 tokens / 256 tokens
+    assert pa.pa_decode_shares(1, 1, 64, 1024, 16, 256) == 64
+    # never more shares than blocks in the bound
+    assert pa.pa_decode_shares(1, 1, 64, 8, 16, 16) == 8
     # rejected shapes size nothing
     assert pa.pa_decode_workspace_bytes(1, 3, 2, 64, 8) == 0
     with pytest.raises(pa.PagedAttentionError):
-        pa.pa_decode_partition_tokens(1, 1, 8, 16, 20)
+        pa.pa_decode_shares(1, 1, 64, 8, 16, 20)
+    with pytest.raises(pa.PagedAttentionError):
+        pa.pa_decode_shares(1, 1, 96, 8)
 
 
 def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
