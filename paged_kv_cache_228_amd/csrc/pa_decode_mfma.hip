@@ -163,15 +163,15 @@ struct MTile {
     typename VChunk<C::VB>::type v[4];
 };
 
-// Issue every load of one tile. valid == false (past the partition) or an id
-// outside the pool gives a zero-byte descriptor: the loads return zeros and
-// touch no memory.
+// Issue every load of one tile. valid == false (past the chunk) or bid < 0
+// (an id outside the pool, marked when staged) gives a zero-byte descriptor:
+// the loads return zeros and touch no memory.
 template <int D, bool I8>
 __device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, int bid, bool valid,
                                       int kvh, int lane)
 {
     using C = MCfg<D, I8>;
-    const bool in_pool = valid && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks;
+    const bool in_pool = valid && bid >= 0;
     const int64_t b = in_pool ? bid : 0;
     const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::TILE;
     const int bytes = in_pool ? C::TILE : 0;
@@ -598,13 +598,14 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             __syncthreads();  // the previous chunk is done with meta
             for (int i = lane; i < nloc; i += 64) {
                 const int bid = a.tables[(int64_t)s * a.max_blocks + jb + i];
+                const bool in_pool = (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks;
                 float ksc = 0.0f, vsc = 0.0f;
-                if (I8 && (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks) {
+                if (I8 && in_pool) {
                     const int64_t si = (int64_t)bid * a.num_kv_heads + kvh;
                     ksc = a.k_scale[si];
                     vsc = a.v_scale[si];
                 }
-                meta[i] = int4{bid, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
+                meta[i] = int4{in_pool ? bid : -1, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
             }
             __syncthreads();
 
@@ -614,24 +615,32 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             // exit, so the last step may compute one empty slot.
             MTile<D, I8> ring[2][SLOT];
             float ks[2][SLOT], vs[2][SLOT];
-            auto load_slot = [&](int r, int j0) {
+            // a slot's meta entries are read from LDS one slot ahead of its loads
+            auto read_meta = [&](int4 (&e)[SLOT], int j0) {
+#pragma unroll
+                for (int u = 0; u < SLOT; ++u) e[u] = meta[j0 + u < nloc ? j0 + u : 0];
+            };
+            auto load_slot = [&](int r, const int4 (&e)[SLOT], int j0) {
 #pragma unroll
                 for (int u = 0; u < SLOT; ++u) {
-                    const int jj = j0 + u;
-                    const int4 e = meta[jj < nloc ? jj : 0];
-                    mload<D, I8>(ring[r][u], a, uniform(e.x), jj < nloc, kvh, lane);
-                    ks[r][u] = __builtin_bit_cast(float, uniform(e.y));
-                    vs[r][u] = __builtin_bit_cast(float, uniform(e.z));
+                    mload<D, I8>(ring[r][u], a, uniform(e[u].x), j0 + u < nloc, kvh, lane);
+                    ks[r][u] = __builtin_bit_cast(float, uniform(e[u].y));
+                    vs[r][u] = __builtin_bit_cast(float, uniform(e[u].z));
                 }
             };
-            load_slot(0, 0);
+            int4 e0[SLOT], e1[SLOT];
+            read_meta(e0, 0);
+            read_meta(e1, SLOT);
+            load_slot(0, e0, 0);
             for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
-                load_slot(1, jj + SLOT);
+                read_meta(e0, jj + 2 * SLOT);
+                load_slot(1, e1, jj + SLOT);
                 __builtin_amdgcn_sched_barrier(0);
                 mslot<D, I8, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0],
                                    lane, lo_sel, kl);
                 __builtin_amdgcn_sched_barrier(0);
-                load_slot(0, jj + 2 * SLOT);
+                read_meta(e1, jj + 3 * SLOT);
+                load_slot(0, e0, jj + 2 * SLOT);
                 __builtin_amdgcn_sched_barrier(0);
                 mslot<D, I8, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2,
                                    ks[1], vs[1], lane, lo_sel, kl);
