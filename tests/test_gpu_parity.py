@@ -123,6 +123,8 @@ def _ragged():
 
 @pytest.mark.parametrize("path", ["f16", "int8"])
 def test_partition_size_invariance(path):
+    # share lengths of 16..4096 tokens and the automatic one; the short ones
+    # give more shares than the batch has tiles
     w = _ragged()
     if path == "int8":
         kc, ks = oracle.quantize_kv_int8(w.k_pool)
@@ -233,3 +235,26 @@ def test_int8_error_against_fp32_is_reported(name):
     assert np.isfinite(rmse)
     if name == "int8_gaussian":
         assert rmse < 1e-2
+
+
+@pytest.mark.parametrize("path", ["f16", "int8"])
+def test_many_short_sequences(path):
+    # more than 1024 sequences (the work split scans them in several passes),
+    # a tenth of them empty (zero rows written by the split's helper groups)
+    rng = np.random.default_rng(703)
+    ctx = rng.integers(1, 200, size=1500)
+    ctx[rng.random(1500) < 0.1] = 0
+    w = W.build("many", 703, ctx, 4, 2, 64, num_blocks=int(((ctx + 15) // 16).sum()) + 8)
+    say(f"many short sequences {path}")
+    if path == "f16":
+        out = decode_f16(w)
+        ref = oracle.decode_workload_f16(w)
+        tol = TOL_F16
+    else:
+        kc, ks = oracle.quantize_kv_int8(w.k_pool)
+        vc, vs = oracle.quantize_kv_int8(w.v_pool)
+        out = decode_int8(w, kc, vc, ks, vs)
+        ref = oracle.decode_workload_int8(w, kc, vc, ks, vs)
+        tol = TOL_I8
+    assert np.max(np.abs(out - ref)) <= tol
+    assert not out[ctx == 0].any()
