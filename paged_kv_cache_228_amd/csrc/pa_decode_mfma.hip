@@ -570,12 +570,33 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     const int qh = n & 7;
     const float lo_sel = n >= 8 ? 1.0f : 0.0f;
 
-    int s = rows[a.num_seqs + 1 + share];  // the row holding tile p0
-    int64_t pos = p0;
-    int j = (int)(p0 - rows[s]);
+    // Segment order: a share's first segment usually starts inside its row;
+    // every later one starts at a row's first block. The later ones go first,
+    // the first one last, so the rows starting in this share are read from
+    // their first block at the start of the decode -- where sequences that
+    // share a prefix keep their common blocks, now read by all of them at
+    // about the same time, which the caches absorb.
+    auto next_row = [&](int r) {  // the next row with tiles (exists while tiles remain)
+        do {
+            ++r;
+        } while (rows[r + 1] == rows[r]);
+        return r;
+    };
+    const int s0 = rows[a.num_seqs + 1 + share];  // the row holding tile p0
+    const int j0 = (int)(p0 - rows[s0]);
+    const int nseg0 = (int)min((int64_t)(rows[s0 + 1] - rows[s0] - j0), p1 - p0);
+    bool deferred = j0 > 0 && p0 + nseg0 < p1;  // the first segment waits for the others
+    int s = deferred ? next_row(s0) : s0;
+    int j = deferred ? 0 : j0;
+    int64_t pos = deferred ? p0 + nseg0 : p0;
     while (true) {
+        const bool last_turn = pos >= p1;  // only the deferred first segment is left
+        if (last_turn) {
+            s = s0;
+            j = j0;
+        }
         const int nblk = rows[s + 1] - rows[s];
-        const int nseg = (int)min((int64_t)(nblk - j), p1 - pos);
+        const int nseg = last_turn ? nseg0 : (int)min((int64_t)(nblk - j), p1 - pos);
         int ctx = a.ctx[s];
         ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : ctx);
 
@@ -648,12 +669,15 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             }
         }
 
-        emit<D, I8>(st, a, s, kvh, group, share, j > 0 || j + nseg < nblk, pos == p0 ? 0 : 1, lane);
+        // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
+        emit<D, I8>(st, a, s, kvh, group, share, j > 0 || j + nseg < nblk, s == s0 && j == j0 ? 0 : 1, lane);
+        if (last_turn) break;
         pos += nseg;
-        if (pos >= p1) break;
-        do {  // the next row with tiles (one exists: pos < p1 <= total)
-            ++s;
-        } while (rows[s + 1] == rows[s]);
+        if (pos >= p1) {
+            if (!deferred) break;
+            continue;  // now the deferred first segment
+        }
+        s = next_row(s);
         j = 0;
     }
 }

@@ -49,35 +49,46 @@ def walk(ctxs, K, max_blocks):
         kf_kl[s] = (share_of(r0, T, K), share_of(r1 - 1, T, K))
     if T:
         assert None not in first_row
-    # decode waves
+    # decode waves: a share's later segments (each from a row's first block)
+    # first, its first segment (which may start mid-row) last
+    def next_row(r):
+        r += 1
+        while rows[r + 1] == rows[r]:
+            r += 1
+        return r
+
     owner, parts, finished = {}, {}, set()
     for k in range(K):
         p0, p1 = k * T // K, (k + 1) * T // K
         if p0 >= p1:
             continue
-        s, pos = first_row[k], p0
-        j = p0 - rows[s]
-        while True:
+        s0 = first_row[k]
+        j0 = p0 - rows[s0]
+        assert 0 <= j0 < nblk[s0]
+        nseg0 = min(nblk[s0] - j0, p1 - p0)
+        segs = []
+        pos, s, j = p0, s0, j0
+        while pos < p1:
+            nseg = min(rows[s + 1] - rows[s] - j, p1 - pos)
+            segs.append((s, j, nseg))
+            pos += nseg
+            if pos < p1:
+                s, j = next_row(s), 0
+        if j0 > 0 and len(segs) > 1:
+            segs = segs[1:] + segs[:1]
+        assert segs[-1 if j0 > 0 and len(segs) > 1 else 0] == (s0, j0, nseg0)
+        for s, j, nseg in segs:
             nb = rows[s + 1] - rows[s]
-            nseg = min(nb - j, p1 - pos)
-            assert nseg > 0
             for t in range(rows[s] + j, rows[s] + j + nseg):
                 assert t not in owner
                 owner[t] = k
             if j > 0 or j + nseg < nb:
-                slot = 0 if pos == p0 else 1
+                slot = 0 if (s, j) == (s0, j0) else 1
                 assert (k, slot) not in parts
                 parts[(k, slot)] = s
             else:
                 assert s not in finished
                 finished.add(s)
-            pos += nseg
-            if pos >= p1:
-                break
-            s += 1
-            while rows[s + 1] == rows[s]:
-                s += 1
-            j = 0
     assert len(owner) == T
     # merge
     for s in range(S):
