@@ -163,16 +163,22 @@ struct MTile {
     typename VChunk<C::VB>::type v[4];
 };
 
-// Issue every load of one tile. valid == false (past the chunk) or bid < 0
-// (an id outside the pool, marked when staged) gives a zero-byte descriptor:
-// the loads return zeros and touch no memory.
+// Issue every load of one tile (and, for INT8, of its K and V scales).
+// valid == false (past the chunk) or bid < 0 (an id outside the pool, marked
+// when staged) gives a zero-byte descriptor: the loads return zeros and touch
+// no memory, and the scales are 0.
 template <int D, bool I8>
 __device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, int bid, bool valid,
-                                      int kvh, int lane)
+                                      int kvh, int lane, float& ksc, float& vsc)
 {
     using C = MCfg<D, I8>;
     const bool in_pool = valid && bid >= 0;
     const int64_t b = in_pool ? bid : 0;
+    if constexpr (I8) {  // uniform addresses: one scalar load each
+        const int64_t si = b * a.num_kv_heads + kvh;
+        ksc = in_pool ? a.k_scale[si] : 0.0f;
+        vsc = in_pool ? a.v_scale[si] : 0.0f;
+    }
     const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::TILE;
     const int bytes = in_pool ? C::TILE : 0;
     const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
@@ -294,28 +300,51 @@ __device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, I8>::KLD]
     }
 }
 
-// Build the query operand of lane (g, n) for head qh (zeros past the group).
+// The raw fp16 query registers of lane (g, n): head qh's dims the lane serves.
 template <int D, bool I8>
-__device__ __forceinline__ void load_q(QOp<D, I8>& qo, const _Float16* qrow, bool live, int g)
+struct QRaw {
+    u32x4 w[I8 ? 2 * MCfg<D, I8>::KLD : MCfg<D, I8>::NQK];
+};
+
+// Issue the query loads of lane (g, n) for head qh (zeros past the group).
+template <int D, bool I8>
+__device__ __forceinline__ void fetch_q(QRaw<D, I8>& qr, const _Float16* qrow, bool live, int g)
+{
+    using C = MCfg<D, I8>;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    if constexpr (I8) {
+        // dims 64c + 16g .. +15: the chunk g + 4c of this lane's K codes
+#pragma unroll
+        for (int c = 0; c < C::KLD; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                qr.w[2 * c + h] = live ? *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g + 8 * h) : z;
+    } else {
+#pragma unroll
+        for (int c = 0; c < C::NQK; ++c)
+            qr.w[c] = live ? *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * c + g)) : z;
+    }
+}
+
+// Build the query operand from the raw registers.
+template <int D, bool I8>
+__device__ __forceinline__ void make_q(QOp<D, I8>& qo, const QRaw<D, I8>& qr)
 {
     using C = MCfg<D, I8>;
     if constexpr (I8) {
-        // dims 64c + 16g .. +15: the chunk g + 4c of this lane's K codes
         float qf[C::KLD][16];
         float mloc = 0.0f;
 #pragma unroll
-        for (int c = 0; c < C::KLD; ++c) {
+        for (int c = 0; c < C::KLD; ++c)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const h8_t v = live ? __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g + 8 * h))
-                                    : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                const h8_t v = __builtin_bit_cast(h8_t, qr.w[2 * c + h]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     qf[c][8 * h + i] = (float)v[i];
                     mloc = fmaxf(mloc, fabsf(qf[c][8 * h + i]));
                 }
             }
-        }
         const float mh = max_over_groups(mloc);  // the four lanes of column n hold all of head n's dims
         const int e = mh > 0.0f ? __builtin_amdgcn_frexp_expf(mh) : 0;  // mh = f 2^e, f in [0.5, 1)
         const float inv = __builtin_ldexpf(1.0f, 6 - e);
@@ -335,13 +364,11 @@ __device__ __forceinline__ void load_q(QOp<D, I8>& qo, const _Float16* qrow, boo
                 w[2][i >> 2] |= ((uint32_t)(int)a3 & 0xFFu) << (8 * (i & 3));
             }
 #pragma unroll
-            for (int j = 0; j < 3; ++j) qo.part[j][c] = u32x4{w[j][0], w[j][1], w[j][2], w[j][3]};
+            for (int jj = 0; jj < 3; ++jj) qo.part[jj][c] = u32x4{w[jj][0], w[jj][1], w[jj][2], w[jj][3]};
         }
     } else {
 #pragma unroll
-        for (int c = 0; c < C::NQK; ++c)
-            qo.b[c] = live ? __builtin_bit_cast(h8_t, *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * c + g)))
-                           : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int c = 0; c < C::NQK; ++c) qo.b[c] = __builtin_bit_cast(h8_t, qr.w[c]);
     }
 }
 
@@ -561,14 +588,15 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     const int64_t p1 = (int64_t)(share + 1) * total / a.shares;
     if (p0 >= p1) return;
 
-    // block ids (and, for INT8, the two scales of each block's tile) of the
-    // current chunk, staged in LDS and read back as a broadcast per tile
-    __shared__ int4 meta[kMaxChunkBlocks];
+    // the current chunk's block ids (ids outside the pool as -1), staged in
+    // LDS and read back as a broadcast per tile
+    __shared__ int mbid[kMaxChunkBlocks];
     __shared__ u32x4 kl[SLOT * MCfg<D, I8>::TILE / 16];  // K of one slot on its way to operand order
     // lane (g, n) serves head n mod 8 of the group; columns 8..15 repeat the
     // group so that rows 8..15 of P can carry the lo halves
     const int qh = n & 7;
     const float lo_sel = n >= 8 ? 1.0f : 0.0f;
+    constexpr int kIdRegs = kMaxChunkBlocks / 64;
 
     // Segment order: a share's first segment usually starts inside its row;
     // every later one starts at a row's first block. The later ones go first,
@@ -579,106 +607,146 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     auto next_row = [&](int r) {  // the next row with tiles (exists while tiles remain)
         do {
             ++r;
-        } while (rows[r + 1] == rows[r]);
+        } while (r < a.num_seqs - 1 && rows[r + 1] == rows[r]);
         return r;
     };
     const int s0 = rows[a.num_seqs + 1 + share];  // the row holding tile p0
     const int j0 = (int)(p0 - rows[s0]);
     const int nseg0 = (int)min((int64_t)(rows[s0 + 1] - rows[s0] - j0), p1 - p0);
-    bool deferred = j0 > 0 && p0 + nseg0 < p1;  // the first segment waits for the others
-    int s = deferred ? next_row(s0) : s0;
-    int j = deferred ? 0 : j0;
-    int64_t pos = deferred ? p0 + nseg0 : p0;
+    const bool deferred = j0 > 0 && p0 + nseg0 < p1;  // the first segment waits for the others
+    int ws = deferred ? next_row(s0) : s0;  // the main walk's next segment
+    int wj = deferred ? 0 : j0;
+    int64_t wpos = deferred ? p0 + nseg0 : p0;
+    bool pending = deferred;
+    struct Seg {
+        int s, j, nseg;
+    };
+    auto take_segment = [&](Seg& sg) {
+        if (wpos < p1) {
+            sg = Seg{ws, wj, (int)min((int64_t)(rows[ws + 1] - rows[ws] - wj), p1 - wpos)};
+            wpos += sg.nseg;
+            if (wpos < p1) {
+                ws = next_row(ws);
+                wj = 0;
+            }
+            return true;
+        }
+        if (pending) {
+            sg = Seg{s0, j0, nseg0};
+            pending = false;
+            return true;
+        }
+        return false;
+    };
+
+    // A chunk is up to kMaxChunkBlocks blocks of one segment. The next
+    // chunk's table entries (and, when it starts a row, that row's query) are
+    // loaded while the current chunk is computed, so switching chunks or rows
+    // does not wait on memory.
+    auto fetch_ids = [&](const Seg& sg, int c0, int (&tb)[kIdRegs]) {
+        const int nloc = min(sg.nseg - c0, kMaxChunkBlocks);
+#pragma unroll
+        for (int r = 0; r < kIdRegs; ++r) {
+            const int i = lane + 64 * r;
+            tb[r] = i < nloc ? a.tables[(int64_t)sg.s * a.max_blocks + sg.j + c0 + i] : -1;
+        }
+    };
+    auto q_row = [&](int row) {
+        return static_cast<const _Float16*>(a.q) + ((int64_t)row * a.num_q_heads + kvh * group + qh) * D;
+    };
+    Seg cg;
+    take_segment(cg);  // the share holds at least one tile
+    int cc0 = 0;
+    int tb[kIdRegs];
+    QRaw<D, I8> qraw;
+    fetch_ids(cg, 0, tb);
+    fetch_q<D, I8>(qraw, q_row(cg.s), qh < group, g);
+    QOp<D, I8> qo;
+    MState<D, I8> st;
     while (true) {
-        const bool last_turn = pos >= p1;  // only the deferred first segment is left
-        if (last_turn) {
-            s = s0;
-            j = j0;
-        }
-        const int nblk = rows[s + 1] - rows[s];
-        const int nseg = last_turn ? nseg0 : (int)min((int64_t)(nblk - j), p1 - pos);
-        int ctx = a.ctx[s];
+        const int nloc = min(cg.nseg - cc0, kMaxChunkBlocks);
+        const int jb = cg.j + cc0;  // first block of the chunk within the row
+        const bool seg_first = cc0 == 0;
+        const bool seg_last = cc0 + kMaxChunkBlocks >= cg.nseg;
+        int ctx = a.ctx[cg.s];
         ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockTokens ? a.max_blocks * kBlockTokens : ctx);
+        // live token rows of the chunk, counted from its first block
+        const int live = min(ctx, (jb + nloc) * kBlockTokens) - jb * kBlockTokens;
 
-        QOp<D, I8> qo;
-        load_q<D, I8>(qo,
-                      static_cast<const _Float16*>(a.q) + ((int64_t)s * a.num_q_heads + kvh * group + qh) * D,
-                      qh < group, g);
-        MState<D, I8> st;
+        __syncthreads();  // the previous chunk is done with mbid
 #pragma unroll
-        for (int nb = 0; nb < MCfg<D, I8>::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        st.m = -INFINITY;
-        st.l = 0.0f;
-        st.vr = 0.0f;
+        for (int r = 0; r < kIdRegs; ++r) {
+            const int i = lane + 64 * r;
+            if (i < nloc) mbid[i] = (uint64_t)(int64_t)tb[r] < (uint64_t)a.num_blocks ? tb[r] : -1;
+        }
+        __syncthreads();
 
-        for (int c0 = 0; c0 < nseg; c0 += kMaxChunkBlocks) {
-            const int jb = j + c0;  // first block of the chunk within the row
-            const int nloc = min(nseg - c0, kMaxChunkBlocks);
-            // live token rows of the chunk, counted from its first block
-            const int live = min(ctx, (jb + nloc) * kBlockTokens) - jb * kBlockTokens;
-            __syncthreads();  // the previous chunk is done with meta
-            for (int i = lane; i < nloc; i += 64) {
-                const int bid = a.tables[(int64_t)s * a.max_blocks + jb + i];
-                const bool in_pool = (uint64_t)(int64_t)bid < (uint64_t)a.num_blocks;
-                float ksc = 0.0f, vsc = 0.0f;
-                if (I8 && in_pool) {
-                    const int64_t si = (int64_t)bid * a.num_kv_heads + kvh;
-                    ksc = a.k_scale[si];
-                    vsc = a.v_scale[si];
-                }
-                meta[i] = int4{in_pool ? bid : -1, __builtin_bit_cast(int, ksc), __builtin_bit_cast(int, vsc), 0};
-            }
-            __syncthreads();
+        // Two-slot ring: one slot is computed while the other's loads are in
+        // flight. Tiles past the chunk load nothing (zero-byte descriptors)
+        // and all their rows are dead; the loop has no early exit, so the last
+        // step may compute one empty slot.
+        MTile<D, I8> ring[2][SLOT];
+        float ks[2][SLOT], vs[2][SLOT];
+        // a slot's ids are read from LDS one slot ahead of its loads
+        auto read_ids = [&](int (&e)[SLOT], int j0_) {
+#pragma unroll
+            for (int u = 0; u < SLOT; ++u) e[u] = mbid[j0_ + u < nloc ? j0_ + u : 0];
+        };
+        auto load_slot = [&](int r, const int (&e)[SLOT], int j0_) {
+#pragma unroll
+            for (int u = 0; u < SLOT; ++u)
+                mload<D, I8>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u], vs[r][u]);
+        };
+        int e0[SLOT], e1[SLOT];
+        read_ids(e0, 0);
+        read_ids(e1, SLOT);
+        load_slot(0, e0, 0);
 
-            // Two-slot ring: one slot is computed while the other's loads are
-            // in flight. Tiles past the chunk load nothing (zero-byte
-            // descriptors) and all their rows are dead; the loop has no early
-            // exit, so the last step may compute one empty slot.
-            MTile<D, I8> ring[2][SLOT];
-            float ks[2][SLOT], vs[2][SLOT];
-            // a slot's meta entries are read from LDS one slot ahead of its loads
-            auto read_meta = [&](int4 (&e)[SLOT], int j0) {
+        if (seg_first) {  // a new row: its query operand and a fresh state
+            make_q<D, I8>(qo, qraw);
 #pragma unroll
-                for (int u = 0; u < SLOT; ++u) e[u] = meta[j0 + u < nloc ? j0 + u : 0];
-            };
-            auto load_slot = [&](int r, const int4 (&e)[SLOT], int j0) {
-#pragma unroll
-                for (int u = 0; u < SLOT; ++u) {
-                    mload<D, I8>(ring[r][u], a, uniform(e[u].x), j0 + u < nloc, kvh, lane);
-                    ks[r][u] = __builtin_bit_cast(float, uniform(e[u].y));
-                    vs[r][u] = __builtin_bit_cast(float, uniform(e[u].z));
-                }
-            };
-            int4 e0[SLOT], e1[SLOT];
-            read_meta(e0, 0);
-            read_meta(e1, SLOT);
-            load_slot(0, e0, 0);
-            for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
-                read_meta(e0, jj + 2 * SLOT);
-                load_slot(1, e1, jj + SLOT);
-                __builtin_amdgcn_sched_barrier(0);
-                mslot<D, I8, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0],
-                                   lane, lo_sel, kl);
-                __builtin_amdgcn_sched_barrier(0);
-                read_meta(e1, jj + 3 * SLOT);
-                load_slot(0, e0, jj + 2 * SLOT);
-                __builtin_amdgcn_sched_barrier(0);
-                mslot<D, I8, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2,
-                                   ks[1], vs[1], lane, lo_sel, kl);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int nb = 0; nb < MCfg<D, I8>::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            st.m = -INFINITY;
+            st.l = 0.0f;
+            st.vr = 0.0f;
+        }
+        // the next chunk: prefetch its ids (and a new row's query)
+        Seg ng = cg;
+        int nc0 = cc0 + kMaxChunkBlocks;
+        bool have_next = true;
+        if (seg_last) {
+            have_next = take_segment(ng);
+            nc0 = 0;
+        }
+        if (have_next) {
+            fetch_ids(ng, nc0, tb);
+            if (nc0 == 0) fetch_q<D, I8>(qraw, q_row(ng.s), qh < group, g);
         }
 
-        // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
-        emit<D, I8>(st, a, s, kvh, group, share, j > 0 || j + nseg < nblk, s == s0 && j == j0 ? 0 : 1, lane);
-        if (last_turn) break;
-        pos += nseg;
-        if (pos >= p1) {
-            if (!deferred) break;
-            continue;  // now the deferred first segment
+        for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
+            read_ids(e0, jj + 2 * SLOT);
+            load_slot(1, e1, jj + SLOT);
+            __builtin_amdgcn_sched_barrier(0);
+            mslot<D, I8, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0], lane,
+                               lo_sel, kl);
+            __builtin_amdgcn_sched_barrier(0);
+            read_ids(e1, jj + 3 * SLOT);
+            load_slot(0, e0, jj + 2 * SLOT);
+            __builtin_amdgcn_sched_barrier(0);
+            mslot<D, I8, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1], vs[1],
+                               lane, lo_sel, kl);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        s = next_row(s);
-        j = 0;
+
+        if (seg_last) {
+            const int nblk = rows[cg.s + 1] - rows[cg.s];
+            // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
+            emit<D, I8>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nblk,
+                        cg.s == s0 && cg.j == j0 ? 0 : 1, lane);
+        }
+        if (!have_next) break;
+        cg = ng;
+        cc0 = nc0;
     }
 }
 
