@@ -55,6 +55,11 @@ def lib() -> C.CDLL:
         L.pa_ref_paged_decode_f16.restype = i32
         L.pa_ref_paged_decode_int8.argtypes = [p, p, p, p, p] + common
         L.pa_ref_paged_decode_int8.restype = i32
+        app = [p, p, i32, i32, i32, i32, i32, i64]
+        L.pa_ref_append_kv_f16.argtypes = [p, p, p, p] + app
+        L.pa_ref_append_kv_f16.restype = i32
+        L.pa_ref_append_kv_int8.argtypes = [p, p, p, p, p, p] + app
+        L.pa_ref_append_kv_int8.restype = i32
         _lib = L
     return _lib
 
@@ -138,3 +143,36 @@ def decode_workload_f16(w, k_pool=None, v_pool=None, **kw):
 def decode_workload_int8(w, k_codes, v_codes, k_scale, v_scale, **kw):
     return paged_decode_int8(w.q, k_codes, v_codes, k_scale, v_scale, w.block_tables,
                              w.context_lens, w.softmax_scale, **kw)
+
+
+def append_kv_f16(k_pool, v_pool, k_new, v_new, block_tables, positions):
+    """New fp16 pools with token ``positions[s]`` of every sequence written
+    (``k_new``/``v_new`` [S][H_kv][d]); the inputs are not modified."""
+    kp = _c(k_pool, np.float16).copy()
+    vp = _c(v_pool, np.float16).copy()
+    nb, h, bs, d = kp.shape
+    kn, vn = _c(k_new, np.float16), _c(v_new, np.float16)
+    tables, pos = _c(block_tables, np.int32), _c(positions, np.int32)
+    rc = lib().pa_ref_append_kv_f16(_ptr(kn.view(np.uint16)), _ptr(vn.view(np.uint16)),
+                                    _ptr(kp.view(np.uint16)), _ptr(vp.view(np.uint16)),
+                                    _ptr(tables), _ptr(pos), pos.size, h, bs, d,
+                                    tables.shape[1], nb)
+    if rc:
+        raise ValueError(f"oracle append failed ({rc})")
+    return kp, vp
+
+
+def append_kv_int8(k_codes, v_codes, k_scale, v_scale, k_new, v_new, block_tables, positions):
+    """New (k_codes, v_codes, k_scale, v_scale) after the INT8 append rule of
+    ``pa_ref_append_kv_int8``; the inputs are not modified."""
+    kc, vc = _c(k_codes, np.int8).copy(), _c(v_codes, np.int8).copy()
+    ks, vs = _c(k_scale, np.float32).copy(), _c(v_scale, np.float32).copy()
+    nb, h, bs, d = kc.shape
+    kn, vn = _c(k_new, np.float16), _c(v_new, np.float16)
+    tables, pos = _c(block_tables, np.int32), _c(positions, np.int32)
+    rc = lib().pa_ref_append_kv_int8(_ptr(kn.view(np.uint16)), _ptr(vn.view(np.uint16)),
+                                     _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(tables),
+                                     _ptr(pos), pos.size, h, bs, d, tables.shape[1], nb)
+    if rc:
+        raise ValueError(f"oracle append failed ({rc})")
+    return kc, vc, ks, vs

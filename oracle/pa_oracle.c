@@ -30,11 +30,15 @@
  *  - scale = amax / 127 in fp32; code = clamp(round-half-even(x / scale),
  *    -127, 127) with an IEEE fp32 division; amax = 0 gives scale 0, codes 0;
  *  - INT8 dequantization is float(code) * scale, one fp32 multiply;
- *  - context length 0 gives an all-zero output row.
+ *  - context length 0 gives an all-zero output row;
+ *  - appending to an INT8 cache re-scales the tile when the new row raises
+ *    its scale (pa_ref_append_kv_int8 states the rule).
  *
  * Parity status: every function here is pinned by the CPU tests (dense
  * fp64 attention on contiguous K/V, invariants, closed forms, exact
- * rational checks of the quantizer, all 65,536 fp16 bit patterns).
+ * rational checks of the quantizer, all 65,536 fp16 bit patterns; the
+ * appends through decode against dense attention, whole-tile quantization
+ * and exact rational re-scaling).
  */
 #include <fenv.h>
 #include <math.h>
@@ -298,4 +302,130 @@ int pa_ref_paged_decode_int8(const uint16_t* q, const int8_t* k_codes, const int
                          context_lens, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
                          block_size, max_blocks_per_seq, num_blocks, softmax_scale, seq_ids,
                          num_seq_ids, weights, weights_stride);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Append: one new token per sequence into the paged cache.                   */
+/* Token t = positions[s] of sequence s goes to block                        */
+/* b = block_tables[s][t / block_size] at slot o = t mod block_size           */
+/* (glossary monograph, section 2.1; PagedAttention article, "Kernel          */
+/* Mechanics": the new K/V are written into the block at                      */
+/* phys_block_id * B + token_offset). A negative position, a position past   */
+/* the table row, or a table entry outside the pool appends nothing.          */
+/* k_new, v_new: fp16 [num_seqs][num_kv_heads][head_dim].                     */
+
+/* The append slot of sequence s, or -1 when it appends nothing. */
+static int64_t append_block(const int32_t* block_tables, const int32_t* positions, int s,
+                            int block_size, int max_blocks_per_seq, int64_t num_blocks, int* slot)
+{
+    int t = positions[s];
+    if (t < 0 || t / block_size >= max_blocks_per_seq) return -1;
+    int64_t b = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+    if (b < 0 || b >= num_blocks) return -1;
+    *slot = t % block_size;
+    return b;
+}
+
+int pa_ref_append_kv_f16(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                         uint16_t* v_pool, const int32_t* block_tables, const int32_t* positions,
+                         int num_seqs, int num_kv_heads, int block_size, int head_dim,
+                         int max_blocks_per_seq, int64_t num_blocks)
+{
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !positions || num_seqs < 0 ||
+        num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return REF_ERR_ARG;
+    for (int s = 0; s < num_seqs; ++s) {
+        int o;
+        int64_t b = append_block(block_tables, positions, s, block_size, max_blocks_per_seq,
+                                 num_blocks, &o);
+        if (b < 0) continue;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            int64_t dst = ((b * num_kv_heads + h) * block_size + o) * head_dim;
+            int64_t src = ((int64_t)s * num_kv_heads + h) * head_dim;
+            for (int j = 0; j < head_dim; ++j) {
+                k_pool[dst + j] = k_new[src + j];
+                v_pool[dst + j] = v_new[src + j];
+            }
+        }
+    }
+    return REF_OK;
+}
+
+/* The quantizer of pa_ref_quantize_kv_int8 for one value at a given scale:
+ * 0 when the scale is 0, else clamp(rint(v / scale), -127, 127). */
+static int8_t quantize_one(float v, float scale)
+{
+    if (scale == 0.0f) return 0;
+    float r = nearbyintf(v / scale);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)((r == r) ? (int)r : 0);
+}
+
+/* INT8 append. The pages define the per-(block, head) symmetric quantizer
+ * (PagedKV-Fusion README, "Overview"; glossary monograph, section 5.1) but
+ * not how a cache that holds only codes takes a new token; the reading used
+ * here keeps the tile quantized with one scale for its live rows:
+ *   x = the new row (head_dim values), s_old = the tile's scale,
+ *   s_new = amax(x) / 127 (fp32, IEEE division);
+ *   o == 0: the block's first token (no live row yet): scale = s_new,
+ *           row 0 = q(x, s_new);
+ *   o > 0, s_new <= s_old: row o = q(x, s_old), scale kept;
+ *   o > 0, s_new >  s_old: the tile grows to s_new: each live row r < o is
+ *           dequantized (code * s_old, one fp32 multiply) and quantized
+ *           again, c = q(code * s_old, s_new); row o = q(x, s_new);
+ *           scale = s_new.
+ * Rows after o are not touched. The same rule runs for K and for V, each
+ * with its own scale. */
+static void append_tile_int8(const uint16_t* x, int8_t* tile, float* scale, int o, int head_dim)
+{
+    float amax = 0.0f;
+    for (int j = 0; j < head_dim; ++j) {
+        float a = fabsf(pa_ref_half_to_float(x[j]));
+        if (a > amax) amax = a;
+    }
+    float s_new = amax / 127.0f;
+    float s_old = *scale;
+    float s = s_new;
+    if (o > 0 && s_new <= s_old) {
+        s = s_old;
+    } else if (o > 0) {
+        for (int r = 0; r < o; ++r)
+            for (int j = 0; j < head_dim; ++j) {
+                float v = (float)tile[(int64_t)r * head_dim + j] * s_old;
+                tile[(int64_t)r * head_dim + j] = quantize_one(v, s_new);
+            }
+    }
+    for (int j = 0; j < head_dim; ++j)
+        tile[(int64_t)o * head_dim + j] = quantize_one(pa_ref_half_to_float(x[j]), s);
+    *scale = s;
+}
+
+int pa_ref_append_kv_int8(const uint16_t* k_new, const uint16_t* v_new, int8_t* k_codes,
+                          int8_t* v_codes, float* k_scale, float* v_scale,
+                          const int32_t* block_tables, const int32_t* positions, int num_seqs,
+                          int num_kv_heads, int block_size, int head_dim, int max_blocks_per_seq,
+                          int64_t num_blocks)
+{
+    if (!k_new || !v_new || !k_codes || !v_codes || !k_scale || !v_scale || !block_tables ||
+        !positions || num_seqs < 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return REF_ERR_ARG;
+    if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+    for (int s = 0; s < num_seqs; ++s) {
+        int o;
+        int64_t b = append_block(block_tables, positions, s, block_size, max_blocks_per_seq,
+                                 num_blocks, &o);
+        if (b < 0) continue;
+        for (int h = 0; h < num_kv_heads; ++h) {
+            int64_t tile = (b * num_kv_heads + h) * block_size * (int64_t)head_dim;
+            int64_t src = ((int64_t)s * num_kv_heads + h) * head_dim;
+            append_tile_int8(k_new + src, k_codes + tile, k_scale + b * num_kv_heads + h, o,
+                             head_dim);
+            append_tile_int8(v_new + src, v_codes + tile, v_scale + b * num_kv_heads + h, o,
+                             head_dim);
+        }
+    }
+    return REF_OK;
 }

@@ -327,6 +327,64 @@ def by_index(idx: int, variant: int | None = None) -> Workload:
     raise ValueError(idx)
 
 
+@dataclass
+class AppendInputs:
+    """One decode step's new tokens: token ``positions[s]`` of sequence s, with
+    K/V rows ``k_new[s]``/``v_new[s]`` ([H_kv][d] fp16 each), goes to block
+    ``block_tables[s][positions[s] // 16]``. ``refcount`` counts the pool's
+    references after the step's block allocations."""
+    block_tables: np.ndarray  # int32 [S][MB'], MB' >= the workload's MB
+    positions: np.ndarray  # int32 [S], -1: the sequence appends nothing
+    k_new: np.ndarray  # fp16 [S][H_kv][d]
+    v_new: np.ndarray
+    refcount: np.ndarray  # int32 [NB]
+
+
+def append_inputs(w: Workload, seed: int, block_tables=None, context_lens=None, refcount=None,
+                  grow_frac: float = 0.0, grow_factor: float = 3.0) -> AppendInputs:
+    """Seeded inputs for appending the next token of every sequence.
+
+    The next token of sequence s is token ``context_lens[s]``. When it starts a
+    new block, a free pool block (refcount 0, picked at random) is added to the
+    sequence's table row, widening the table by a column if needed. A sequence
+    whose next slot lies in a block other sequences also read (refcount > 1)
+    would need a private copy first; it appends nothing (position -1). New rows
+    are N(0, 1) in fp16; a ``grow_frac`` share of the (sequence, KV head) rows
+    is multiplied by ``grow_factor`` (for an INT8 cache, rows that raise their
+    tile's scale). Pass the previous step's tables, contexts and refcounts to
+    chain steps."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(17,)))
+    tables = np.array(w.block_tables if block_tables is None else block_tables, dtype=np.int32)
+    ctx = np.array(w.context_lens if context_lens is None else context_lens, dtype=np.int64)
+    ref = np.array(w.refcount if refcount is None else refcount, dtype=np.int32)
+    S = tables.shape[0]
+    positions = np.full(S, -1, dtype=np.int32)
+    for s in range(S):
+        t = int(ctx[s])
+        j, o = divmod(t, BLOCK_SIZE)
+        if j >= tables.shape[1]:
+            tables = np.concatenate([tables, np.full((S, 1), -1, np.int32)], axis=1)
+        if o == 0:
+            free = np.flatnonzero(ref == 0)
+            if free.size == 0:
+                raise MemoryError("KV block pool exhausted")
+            b = int(free[rng.integers(free.size)])
+            ref[b] = 1
+            tables[s, j] = b
+        elif ref[tables[s, j]] > 1:
+            continue
+        positions[s] = t
+    hkv, d = w.num_kv_heads, w.head_dim
+    k_new = rng.standard_normal((S, hkv, d), dtype=np.float32)
+    v_new = rng.standard_normal((S, hkv, d), dtype=np.float32)
+    if grow_frac > 0:
+        for x in (k_new, v_new):
+            x[rng.random((S, hkv)) < grow_frac] *= np.float32(grow_factor)
+    return AppendInputs(block_tables=tables, positions=positions,
+                        k_new=k_new.astype(np.float16), v_new=v_new.astype(np.float16),
+                        refcount=ref)
+
+
 def algorithmic_bytes(w: Workload, kv_bytes_per_elem: int, with_scales: bool) -> int:
     """Bytes the decode step must move: each distinct live (block, head) slot's
     K and V once, INT8 scales once per distinct (block, head), one int32 per
@@ -348,5 +406,5 @@ def logical_kv_tokens(w: Workload) -> int:
 __all__ = [
     "BLOCK_SIZE", "BlockAllocator", "Workload", "build", "from_contiguous", "tiny",
     "qwen2_layer", "int8_gaussian", "int8_heavy_tailed", "mixed_prefix", "by_index",
-    "algorithmic_bytes", "logical_kv_tokens",
+    "algorithmic_bytes", "logical_kv_tokens", "AppendInputs", "append_inputs",
 ]
