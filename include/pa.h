@@ -135,6 +135,49 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          float softmax_scale, int partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Append one new token per sequence to a paged cache (the step before a
+ * decode). Token t = positions[s] of sequence s goes to physical block
+ * block_tables[s][t / 16] at slot t mod 16 (glossary monograph, section 2.1;
+ * PagedAttention article, "Kernel Mechanics": new K/V are written at
+ * phys_block_id * B + token_offset). A negative position, a position past the
+ * table row (t / 16 >= max_blocks_per_seq) or a table entry outside
+ * [0, num_blocks) appends nothing for that sequence; other device data is not
+ * validated.
+ *  k_new, v_new: fp16 [num_seqs][num_kv_heads][head_dim], the new token's rows
+ *  k_cache, v_cache: [num_blocks][num_kv_heads][16][head_dim], updated in place
+ *  block_tables: int32 [num_seqs][max_blocks_per_seq]; positions: int32 [num_seqs]
+ * All pointers are device pointers owned by the caller; every buffer starts on
+ * a 16-byte boundary. Two sequences must not append into the same block in one
+ * call. One asynchronous kernel on `stream`; nothing is allocated.
+ * Returns PA_OK (also for num_seqs == 0), PA_ERR_NULL, PA_ERR_SHAPE,
+ * PA_ERR_UNSUPPORTED (block_size != 16, head_dim not 64 or 128, more than
+ * 65,535 sequences or KV heads, misaligned buffers) or PA_ERR_HIP.
+ *
+ * pa_append_kv_f16 copies the rows into the fp16 cache. */
+int pa_append_kv_f16(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* positions, int num_seqs,
+                     int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                     int64_t num_blocks, void* stream);
+
+/* pa_append_kv_int8 appends to an INT8 cache with one fp32 scale per (block,
+ * KV head) for K and one for V (the layout pa_quantize_kv_int8 writes). The
+ * pages fix the quantizer (PagedKV-Fusion README, "Overview": symmetric INT8
+ * per (block, head); glossary monograph, section 5.1: code = round(x / S))
+ * but not how a codes-only cache takes a new token; the rule here keeps one
+ * scale per tile for its live rows. With x the new row, o = t mod 16, s_old
+ * the tile's scale and s_new = max|x| / 127 (IEEE fp32 division):
+ *   o == 0:                the block's first token: scale = s_new, row 0 = q(x, s_new)
+ *   o > 0, s_new <= s_old: row o = q(x, s_old), scale kept
+ *   o > 0, s_new >  s_old: rows r < o re-quantized as q(code * s_old, s_new)
+ *                          (fp32 product), row o = q(x, s_new), scale = s_new
+ * q(v, s) = 0 if s == 0, else clamp(round-half-even(v / s), -127, 127) with
+ * an IEEE fp32 division. Rows after o are not touched.
+ *  k_scale, v_scale: fp32 [num_blocks][num_kv_heads], updated in place */
+int pa_append_kv_int8(const void* k_new, const void* v_new, int8_t* k_cache, int8_t* v_cache,
+                      float* k_scale, float* v_scale, const int32_t* block_tables,
+                      const int32_t* positions, int num_seqs, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int64_t num_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

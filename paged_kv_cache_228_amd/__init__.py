@@ -39,6 +39,8 @@ EXPORTED = (
     "pa_decode_shares",
     "pa_paged_decode_f16",
     "pa_paged_decode_int8",
+    "pa_append_kv_f16",
+    "pa_append_kv_int8",
 )
 
 
@@ -73,6 +75,11 @@ def lib() -> C.CDLL:
         L.pa_paged_decode_f16.restype = i32
         L.pa_paged_decode_int8.argtypes = [p, p, p, p, p] + tail
         L.pa_paged_decode_int8.restype = i32
+        app = [p, p, i32, i32, i32, i32, i32, i64, p]
+        L.pa_append_kv_f16.argtypes = [p, p, p, p] + app
+        L.pa_append_kv_f16.restype = i32
+        L.pa_append_kv_int8.argtypes = [p, p, p, p, p, p] + app
+        L.pa_append_kv_int8.restype = i32
         _lib = L
     return _lib
 
@@ -209,8 +216,58 @@ def pa_paged_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables, co
         raise PagedAttentionError("pa_paged_decode_int8", rc)
 
 
+def _append_args(k_new, v_new, k_cache, block_tables, positions):
+    import torch
+
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(positions, "positions", torch.int32, 1)
+    nb, hkv, bs, d = k_cache.shape
+    S = k_new.shape[0]
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError("k_new / v_new must be [num_seqs][num_kv_heads][head_dim] of the cache")
+    if block_tables.shape[0] != S or positions.shape[0] != S:
+        raise ValueError("block_tables / positions rows must match num_seqs")
+    return S, hkv, d, bs, block_tables.shape[1], nb
+
+
+def pa_append_kv_f16(k_new, v_new, k_cache, v_cache, block_tables, positions, stream=None):
+    """Write token ``positions[s]`` of every sequence into the fp16 cache."""
+    import torch
+
+    _need(k_cache, "k_cache", torch.float16, 4)
+    _need(v_cache, "v_cache", torch.float16, 4)
+    S, hkv, d, bs, mb, nb = _append_args(k_new, v_new, k_cache, block_tables, positions)
+    rc = lib().pa_append_kv_f16(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_tables), _ptr(positions), S, hkv, d, bs, mb, nb,
+                                _stream(k_cache, stream))
+    if rc:
+        raise PagedAttentionError("pa_append_kv_f16", rc)
+
+
+def pa_append_kv_int8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, positions,
+                      stream=None):
+    """Append token ``positions[s]`` of every sequence to the INT8 cache,
+    re-scaling a tile whose scale the new row raises."""
+    import torch
+
+    _need(k_cache, "k_cache", torch.int8, 4)
+    _need(v_cache, "v_cache", torch.int8, 4)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    _need(v_scale, "v_scale", torch.float32, 2)
+    S, hkv, d, bs, mb, nb = _append_args(k_new, v_new, k_cache, block_tables, positions)
+    rc = lib().pa_append_kv_int8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                 _ptr(positions), S, hkv, d, bs, mb, nb,
+                                 _stream(k_cache, stream))
+    if rc:
+        raise PagedAttentionError("pa_append_kv_int8", rc)
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
-    "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8",
+    "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
+    "pa_append_kv_int8",
 ]

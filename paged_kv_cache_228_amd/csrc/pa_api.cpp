@@ -126,6 +126,39 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
+int append_common(const void* k_new, const void* v_new, void* k_cache, void* v_cache, float* ks,
+                  float* vs, const int32_t* tables, const int32_t* positions, int num_seqs,
+                  int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                  int64_t num_blocks, void* stream, bool int8)
+{
+    if (!k_new || !v_new || !k_cache || !v_cache || !tables || !positions) return PA_ERR_NULL;
+    if (int8 && (!ks || !vs)) return PA_ERR_NULL;
+    if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return PA_ERR_SHAPE;
+    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    pa::AppendArgs a;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.k = k_cache;
+    a.v = v_cache;
+    a.ks = ks;
+    a.vs = vs;
+    a.tables = tables;
+    a.positions = positions;
+    a.num_blocks = num_blocks;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    hipError_t e = pa::launch_append(a, head_dim, int8, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,6 +259,26 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
                          workspace, workspace_bytes, stream, true);
+}
+
+int pa_append_kv_f16(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     const int32_t* block_tables, const int32_t* positions, int num_seqs,
+                     int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                     int64_t num_blocks, void* stream)
+{
+    return append_common(k_new, v_new, k_cache, v_cache, nullptr, nullptr, block_tables, positions,
+                         num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                         num_blocks, stream, false);
+}
+
+int pa_append_kv_int8(const void* k_new, const void* v_new, int8_t* k_cache, int8_t* v_cache,
+                      float* k_scale, float* v_scale, const int32_t* block_tables,
+                      const int32_t* positions, int num_seqs, int num_kv_heads, int head_dim,
+                      int block_size, int max_blocks_per_seq, int64_t num_blocks, void* stream)
+{
+    return append_common(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                         positions, num_seqs, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, stream, true);
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI front end (pa_api.cpp) and the HIP
-// kernels (pa_decode.hip, pa_quantize.hip). Not installed; not part of the ABI.
+// kernels (pa_decode.hip, pa_decode_mfma.hip, pa_quantize.hip, pa_append.hip). Not
+// installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,5 +79,23 @@ struct QuantArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t st);
+
+// One new token per sequence into the paged cache (pa_append.hip).
+struct AppendArgs {
+    const uint16_t* k_new;    // fp16 [S][Hkv][D]
+    const uint16_t* v_new;
+    void* k;                  // fp16 or int8 pool [NB][Hkv][16][D]
+    void* v;
+    float* ks;                // INT8 only: [NB][Hkv]
+    float* vs;
+    const int32_t* tables;    // [S][max_blocks]
+    const int32_t* positions; // [S]
+    int64_t num_blocks;
+    int num_seqs;
+    int num_kv_heads;
+    int max_blocks;
+};
+
+hipError_t launch_append(const AppendArgs& a, int head_dim, bool int8, hipStream_t st);
 
 }  // namespace pa

@@ -108,6 +108,46 @@ def test_quantize_rejects_bad_arguments_on_host():
     assert q(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 2, 16, 64, None) == pa.PA_OK
 
 
+def append_call(int8, **over):
+    args = dict(kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, t=FAKE, p=FAKE, S=2, hkv=2,
+                d=64, bs=16, mb=5, nb=16)
+    args.update(over)
+    a = args
+    tail = (a["t"], a["p"], a["S"], a["hkv"], a["d"], a["bs"], a["mb"], a["nb"], None)
+    if int8:
+        return pa.lib().pa_append_kv_int8(a["kn"], a["vn"], a["k"], a["v"], a["ks"], a["vs"], *tail)
+    return pa.lib().pa_append_kv_f16(a["kn"], a["vn"], a["k"], a["v"], *tail)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+@pytest.mark.parametrize(
+    "over,code",
+    [
+        (dict(kn=None), pa.PA_ERR_NULL),
+        (dict(v=None), pa.PA_ERR_NULL),
+        (dict(t=None), pa.PA_ERR_NULL),
+        (dict(p=None), pa.PA_ERR_NULL),
+        (dict(S=-1), pa.PA_ERR_SHAPE),
+        (dict(hkv=0), pa.PA_ERR_SHAPE),
+        (dict(mb=0), pa.PA_ERR_SHAPE),
+        (dict(nb=0), pa.PA_ERR_SHAPE),
+        (dict(bs=8), pa.PA_ERR_UNSUPPORTED),
+        (dict(d=96), pa.PA_ERR_UNSUPPORTED),
+        (dict(S=70000), pa.PA_ERR_UNSUPPORTED),
+        (dict(k=FAKE + 4), pa.PA_ERR_UNSUPPORTED),
+        (dict(vn=FAKE + 2), pa.PA_ERR_UNSUPPORTED),
+        (dict(S=0), pa.PA_OK),  # nothing to append, nothing launched
+    ],
+)
+def test_append_rejects_bad_arguments_on_host(int8, over, code):
+    assert append_call(int8, **over) == code
+
+
+def test_int8_append_needs_scales():
+    assert append_call(True, ks=None) == pa.PA_ERR_NULL
+    assert append_call(False, ks=None, vs=None, S=0) == pa.PA_OK
+
+
 def test_workspace_and_share_sizing():
     # Without a device to ask, the library sizes for 256 compute units.
     # A tiny batch: at most one share per 8 blocks of the 2 x 5-block bound.
