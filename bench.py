@@ -14,7 +14,9 @@ context ~ U[512, 16384], 32 query heads / 8 KV heads, head_dim 128, groups of
 Prints one JSON line. `value` is context (KV) tokens attended per second over
 the step (both decodes: 2 x sum(ctx) per step); the per-call figures, the
 roofline of the dominant call and the oracle's CPU time on the same step are
-in the same line.
+in the same line. After the timed steps the next token's append
+(pa_append_kv_f16 / pa_append_kv_int8) is timed on its own and reported
+under `paths`; it is not part of the step.
 """
 
 import argparse
@@ -61,6 +63,8 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and output check)")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip timing the next-token append calls after the step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes "
                          "(a known-size reference for HBM byte counters)")
@@ -225,6 +229,55 @@ def main() -> int:
             "fp16_max_abs": float(np.max(np.abs(out16_h - ref16))),
             "int8_max_abs": float(np.max(np.abs(out8_h - ref8))),
         }
+    # The append of the next token (timed on its own after the step, not part
+    # of it): every sequence writes one K and one V row, fp16 and INT8.
+    if not args.no_append:
+        app = W.append_inputs(w, w.seed + 1, grow_frac=0.25)
+        a_tab, a_pos = up(app.block_tables), up(app.positions)
+        a_k, a_v = up(app.k_new), up(app.v_new)
+        calls = {
+            "append_f16": lambda: pa.pa_append_kv_f16(a_k, a_v, k16, v16, a_tab, a_pos),
+            "append_int8": lambda: pa.pa_append_kv_int8(a_k, a_v, k8, v8, ks, vs, a_tab, a_pos),
+        }
+        n_app = int((app.positions >= 0).sum())
+        row = hkv * d
+        app_alg = {
+            # new K/V rows read and written, one table entry and position per sequence
+            "append_f16": n_app * row * 2 * 2 * 2 + S * 8,
+            # + per (block, head) two scales read and written; the INT8 rows are written
+            "append_int8": n_app * row * 2 * (2 + 1) + n_app * hkv * 2 * 8 + S * 8,
+        }
+        for name, fn in calls.items():
+            for _ in range(5):
+                fn()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            e[0].record()
+            for _ in range(200):
+                fn()
+            e[1].record()
+            torch.cuda.synchronize()
+            us = e[0].elapsed_time(e[1]) * 1e3 / 200
+            paths[name] = {"us": round(us, 3), "alg_bytes": app_alg[name],
+                           "gbs": round(app_alg[name] / us / 1e3, 1), "sequences": n_app,
+                           "note": "launch-bound: a few hundred bytes per (sequence, KV head)"}
+        if not args.no_cpu_baseline:
+            import oracle
+
+            ok, ov = oracle.append_kv_f16(w.k_pool, w.v_pool, app.k_new, app.v_new,
+                                          app.block_tables, app.positions)
+            touched = np.unique(app.block_tables[np.arange(S), np.maximum(app.positions, 0) // 16]
+                                [app.positions >= 0])
+            tix = up(touched.astype(np.int64))
+            gk, gv = k16[tix].cpu().numpy(), v16[tix].cpu().numpy()
+            o8 = oracle.append_kv_int8(okc, ovc, oks, ovs, app.k_new, app.v_new,
+                                       app.block_tables, app.positions)
+            g8 = [x[tix].cpu().numpy() for x in (k8, v8, ks, vs)]
+            result["parity"]["append_bit_exact"] = bool(
+                np.array_equal(gk.view(np.uint16), ok[touched].view(np.uint16))
+                and np.array_equal(gv.view(np.uint16), ov[touched].view(np.uint16))
+                and all(np.array_equal(g.view(np.uint8), r[touched].view(np.uint8))
+                        for g, r in zip(g8, o8)))
     print(json.dumps(result), flush=True)
     return 0
 

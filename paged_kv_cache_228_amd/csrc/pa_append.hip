@@ -48,26 +48,29 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a)
     constexpr int EPL = D / 64;  // elements of the row per lane
     const int h = blockIdx.x, s = blockIdx.y;
     const int tensor = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the new row does not depend on the slot: its load goes out with the
+    // position's, before the table entry that the position selects
+    const uint16_t* src = (tensor ? a.v_new : a.k_new) + ((int64_t)s * a.num_kv_heads + h) * D + lane * EPL;
+    uint32_t raw = EPL == 2 ? *reinterpret_cast<const uint32_t*>(src) : (uint32_t)*src;
     const int t = a.positions[s];
     if (t < 0 || t / kBlockTokens >= a.max_blocks) return;
     const int64_t b = a.tables[(int64_t)s * a.max_blocks + t / kBlockTokens];
     if (b < 0 || b >= a.num_blocks) return;
     const int o = t % kBlockTokens;
     const int64_t tile = (b * a.num_kv_heads + h) * (int64_t)(kBlockTokens * D);
-    const uint16_t* src = (tensor ? a.v_new : a.k_new) + ((int64_t)s * a.num_kv_heads + h) * D + lane * EPL;
 
     if (!I8) {
         uint16_t* dst = static_cast<uint16_t*>(tensor ? a.v : a.k) + tile + o * D + lane * EPL;
         if (EPL == 2)
-            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+            *reinterpret_cast<uint32_t*>(dst) = raw;
         else
-            *dst = *src;
+            *dst = (uint16_t)raw;
         return;
     }
 
     float x[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = (float)__builtin_bit_cast(_Float16, src[e]);
+    for (int e = 0; e < EPL; ++e) x[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw >> (16 * e)));
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
