@@ -135,6 +135,25 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          float softmax_scale, int partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Choose the physical blocks to evict (PagedKV-Fusion README, "Overview",
+ * component A: scoring plus a top-k over the paged blocks, the "bottom-k
+ * eviction ids" of its sequence diagram). Scores follow the PagedAttention &
+ * KV-Cache Memory Management monograph, section 4.3.1 (least reference count
+ * plus age): over the allocated blocks (refcount > 0),
+ *     score = 0.7 (max_refcnt - refcount[b]) + 0.3 (current_tick - last_used[b])
+ * with max_refcnt the largest reference count among them; a higher score is a
+ * better block to evict. out_ids receives the min(k, candidates) blocks with
+ * the largest scores (equal scores: the smaller block id first) in ascending
+ * id order, then -1 up to k. The order is computed exactly (integer keys, no
+ * rounding).
+ *  refcount, last_used: int32 [num_blocks] (device); out_ids: int32 [k] (device)
+ * One asynchronous single-workgroup kernel on `stream`; nothing is allocated.
+ * Returns PA_OK (k == 0 launches nothing), PA_ERR_NULL, PA_ERR_SHAPE
+ * (num_blocks <= 0, k < 0), PA_ERR_UNSUPPORTED (more than 2^31 - 1 blocks or
+ * ids, misaligned buffers) or PA_ERR_HIP. */
+int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t num_blocks,
+                    int32_t current_tick, int64_t k, int32_t* out_ids, void* stream);
+
 /* Append one new token per sequence to a paged cache (the step before a
  * decode). Token t = positions[s] of sequence s goes to physical block
  * block_tables[s][t / 16] at slot t mod 16 (glossary monograph, section 2.1;

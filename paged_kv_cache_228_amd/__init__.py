@@ -41,6 +41,7 @@ EXPORTED = (
     "pa_paged_decode_int8",
     "pa_append_kv_f16",
     "pa_append_kv_int8",
+    "pa_evict_select",
 )
 
 
@@ -80,6 +81,8 @@ def lib() -> C.CDLL:
         L.pa_append_kv_f16.restype = i32
         L.pa_append_kv_int8.argtypes = [p, p, p, p, p, p] + app
         L.pa_append_kv_int8.restype = i32
+        L.pa_evict_select.argtypes = [p, p, i64, i32, i64, p, p]
+        L.pa_evict_select.restype = i32
         _lib = L
     return _lib
 
@@ -265,9 +268,32 @@ def pa_append_kv_int8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_ta
         raise PagedAttentionError("pa_append_kv_int8", rc)
 
 
+def pa_evict_select(refcount, last_used, current_tick, k, out_ids=None, stream=None):
+    """Ids (ascending, -1 padded to k) of the k blocks least worth keeping by
+    reference count and age; returns ``out_ids`` (allocated if not given)."""
+    import torch
+
+    _need(refcount, "refcount", torch.int32, 1)
+    _need(last_used, "last_used", torch.int32, 1)
+    if last_used.numel() != refcount.numel():
+        raise ValueError("refcount and last_used must have one entry per block")
+    if out_ids is None:
+        out_ids = torch.empty(max(int(k), 0), dtype=torch.int32, device=refcount.device)
+    else:
+        _need(out_ids, "out_ids", torch.int32, 1)
+        if out_ids.numel() < k:
+            raise ValueError("out_ids holds fewer than k ids")
+    rc = lib().pa_evict_select(_ptr(refcount), _ptr(last_used), refcount.numel(),
+                               int(current_tick), int(k), _ptr(out_ids),
+                               _stream(refcount, stream))
+    if rc:
+        raise PagedAttentionError("pa_evict_select", rc)
+    return out_ids
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
-    "pa_append_kv_int8",
+    "pa_append_kv_int8", "pa_evict_select",
 ]

@@ -261,6 +261,26 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          workspace, workspace_bytes, stream, true);
 }
 
+int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t num_blocks,
+                    int32_t current_tick, int64_t k, int32_t* out_ids, void* stream)
+{
+    if (!refcount || !last_used || (k > 0 && !out_ids)) return PA_ERR_NULL;
+    if (num_blocks <= 0 || k < 0) return PA_ERR_SHAPE;
+    if (num_blocks > 0x7fffffffLL || k > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(refcount) | reinterpret_cast<uintptr_t>(last_used) |
+         reinterpret_cast<uintptr_t>(out_ids)) & 3u)
+        return PA_ERR_UNSUPPORTED;
+    pa::EvictArgs a;
+    a.refcount = refcount;
+    a.last_used = last_used;
+    a.out = out_ids;
+    a.num_blocks = num_blocks;
+    a.k = k;
+    a.tick = current_tick;
+    hipError_t e = pa::launch_evict(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
 int pa_append_kv_f16(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                      const int32_t* block_tables, const int32_t* positions, int num_seqs,
                      int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,

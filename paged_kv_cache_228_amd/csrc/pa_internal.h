@@ -1,6 +1,6 @@
 // Internal interface between the C-ABI front end (pa_api.cpp) and the HIP
-// kernels (pa_decode.hip, pa_decode_mfma.hip, pa_quantize.hip, pa_append.hip). Not
-// installed; not part of the ABI.
+// kernels (pa_decode.hip, pa_decode_mfma.hip, pa_quantize.hip, pa_append.hip,
+// pa_evict.hip). Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -97,5 +97,17 @@ struct AppendArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, int head_dim, bool int8, hipStream_t st);
+
+// Eviction choice over the physical blocks (pa_evict.hip).
+struct EvictArgs {
+    const int32_t* refcount;   // [num_blocks]
+    const int32_t* last_used;  // [num_blocks]
+    int32_t* out;              // [k]
+    int64_t num_blocks;
+    int64_t k;
+    int32_t tick;
+};
+
+hipError_t launch_evict(const EvictArgs& a, hipStream_t st);
 
 }  // namespace pa

@@ -385,6 +385,25 @@ def append_inputs(w: Workload, seed: int, block_tables=None, context_lens=None, 
                         refcount=ref)
 
 
+def eviction_inputs(num_blocks: int, seed: int, current_tick: int = 10_000,
+                    free_frac: float = 0.2, refcount=None):
+    """Seeded block metadata for the eviction choice: int32 reference counts
+    (``free_frac`` of the blocks free, most of the rest held once, some
+    shared by 2-4 sequences; or the given ``refcount``) and int32 ticks of
+    last use, uniform over [0, current_tick] for allocated blocks, 0 for free
+    ones."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(23,)))
+    if refcount is None:
+        ref = np.where(rng.random(num_blocks) < 0.85, 1, rng.integers(2, 5, size=num_blocks))
+        ref[rng.random(num_blocks) < free_frac] = 0
+    else:
+        ref = np.asarray(refcount)
+    ref = ref.astype(np.int32)
+    last = rng.integers(0, current_tick + 1, size=num_blocks).astype(np.int32)
+    last[ref == 0] = 0
+    return ref, last
+
+
 def algorithmic_bytes(w: Workload, kv_bytes_per_elem: int, with_scales: bool) -> int:
     """Bytes the decode step must move: each distinct live (block, head) slot's
     K and V once, INT8 scales once per distinct (block, head), one int32 per
@@ -407,4 +426,5 @@ __all__ = [
     "BLOCK_SIZE", "BlockAllocator", "Workload", "build", "from_contiguous", "tiny",
     "qwen2_layer", "int8_gaussian", "int8_heavy_tailed", "mixed_prefix", "by_index",
     "algorithmic_bytes", "logical_kv_tokens", "AppendInputs", "append_inputs",
+    "eviction_inputs",
 ]

@@ -148,6 +148,23 @@ def test_int8_append_needs_scales():
     assert append_call(False, ks=None, vs=None, S=0) == pa.PA_OK
 
 
+@pytest.mark.parametrize(
+    "args,code",
+    [
+        ((None, FAKE, 16, 5, 3, FAKE), pa.PA_ERR_NULL),
+        ((FAKE, None, 16, 5, 3, FAKE), pa.PA_ERR_NULL),
+        ((FAKE, FAKE, 16, 5, 3, None), pa.PA_ERR_NULL),
+        ((FAKE, FAKE, 0, 5, 3, FAKE), pa.PA_ERR_SHAPE),
+        ((FAKE, FAKE, 16, 5, -1, FAKE), pa.PA_ERR_SHAPE),
+        ((FAKE, FAKE, 2**31, 5, 3, FAKE), pa.PA_ERR_UNSUPPORTED),
+        ((FAKE + 2, FAKE, 16, 5, 3, FAKE), pa.PA_ERR_UNSUPPORTED),
+        ((FAKE, FAKE, 16, 5, 0, None), pa.PA_OK),  # k == 0: nothing launched
+    ],
+)
+def test_evict_rejects_bad_arguments_on_host(args, code):
+    assert pa.lib().pa_evict_select(*args, None) == code
+
+
 def test_workspace_and_share_sizing():
     # Without a device to ask, the library sizes for 256 compute units.
     # A tiny batch: at most one share per 8 blocks of the 2 x 5-block bound.
