@@ -15,8 +15,10 @@ Prints one JSON line. `value` is context (KV) tokens attended per second over
 the step (both decodes: 2 x sum(ctx) per step); the per-call figures, the
 roofline of the dominant call and the oracle's CPU time on the same step are
 in the same line. After the timed steps the next token's append
-(pa_append_kv_f16 / pa_append_kv_int8) is timed on its own and reported
-under `paths`; it is not part of the step.
+(pa_append_kv_f16 / pa_append_kv_int8) and the eviction choice
+(pa_evict_select, 15 % of the allocated blocks at 1,024, 16,384 and 65,536
+blocks) are timed on their own and reported under `paths`; neither is part
+of the step.
 """
 
 import argparse
@@ -63,6 +65,8 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and output check)")
+    ap.add_argument("--no-evict", action="store_true",
+                    help="skip timing the eviction choice after the step")
     ap.add_argument("--no-append", action="store_true",
                     help="skip timing the next-token append calls after the step")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -278,6 +282,36 @@ def main() -> int:
                 and np.array_equal(gv.view(np.uint16), ov[touched].view(np.uint16))
                 and all(np.array_equal(g.view(np.uint8), r[touched].view(np.uint8))
                         for g, r in zip(g8, o8)))
+    # The eviction choice (timed on its own, not part of the step): 15 % of
+    # the allocated blocks, at the README's pool sizes and on this batch's pool
+    # with its reference counts; p50 of per-call event times like the README.
+    if not args.no_evict:
+        ev = {}
+        for nb_ev in (1024, 16384, w.num_blocks):
+            ref_h, last_h = W.eviction_inputs(nb_ev, 50 + nb_ev,
+                                              refcount=w.refcount if nb_ev == w.num_blocks else None)
+            k_ev = (int((ref_h > 0).sum()) * 15) // 100
+            ref_d, last_d = up(ref_h), up(last_h)
+            out_d = torch.empty(max(k_ev, 1), dtype=torch.int32, device=dev)
+            for _ in range(10):
+                pa.pa_evict_select(ref_d, last_d, 10_000, k_ev, out_d)
+            times = []
+            for _ in range(200):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                pa.pa_evict_select(ref_d, last_d, 10_000, k_ev, out_d)
+                e[1].record()
+                e[1].synchronize()
+                times.append(e[0].elapsed_time(e[1]) * 1e3)
+            rec = {"blocks": nb_ev, "evict": k_ev, "p50_us": round(float(np.median(times)), 2),
+                   "p90_us": round(float(np.percentile(times, 90)), 2)}
+            if not args.no_cpu_baseline:
+                import oracle.evict as OE
+
+                got = out_d[:k_ev].cpu().numpy()
+                rec["bit_exact"] = bool(np.array_equal(got, OE.evict_select(ref_h, last_h, 10_000, k_ev)))
+            ev[str(nb_ev)] = rec
+        paths["evict_select"] = ev
     print(json.dumps(result), flush=True)
     return 0
 

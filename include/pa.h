@@ -146,7 +146,8 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
  * the largest scores (equal scores: the smaller block id first) in ascending
  * id order, then -1 up to k. The order is computed exactly (integer keys, no
  * rounding).
- *  refcount, last_used: int32 [num_blocks] (device); out_ids: int32 [k] (device)
+ *  refcount, last_used: int32 [num_blocks] (device, 16-byte aligned);
+ *  out_ids: int32 [k] (device)
  * One asynchronous single-workgroup kernel on `stream`; nothing is allocated.
  * Returns PA_OK (k == 0 launches nothing), PA_ERR_NULL, PA_ERR_SHAPE
  * (num_blocks <= 0, k < 0), PA_ERR_UNSUPPORTED (more than 2^31 - 1 blocks or

@@ -267,8 +267,8 @@ int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t n
     if (!refcount || !last_used || (k > 0 && !out_ids)) return PA_ERR_NULL;
     if (num_blocks <= 0 || k < 0) return PA_ERR_SHAPE;
     if (num_blocks > 0x7fffffffLL || k > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    if ((reinterpret_cast<uintptr_t>(refcount) | reinterpret_cast<uintptr_t>(last_used) |
-         reinterpret_cast<uintptr_t>(out_ids)) & 3u)
+    if (((reinterpret_cast<uintptr_t>(refcount) | reinterpret_cast<uintptr_t>(last_used)) & 15u) ||
+        (reinterpret_cast<uintptr_t>(out_ids) & 3u))
         return PA_ERR_UNSUPPORTED;
     pa::EvictArgs a;
     a.refcount = refcount;

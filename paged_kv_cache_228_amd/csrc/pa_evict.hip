@@ -19,8 +19,9 @@
 //      with a 256-bin histogram in LDS;
 //   3. one pass in block order: keys above the threshold, plus the first
 //      (by id) of those equal to it until k' are chosen; block-wide prefix
-//      counts (wave ballots) give each chosen id its output slot.
-// The block metadata (8 bytes per block) is re-read per pass from the cache.
+//      sums of per-thread counts give each chosen id its output slot.
+// Each thread takes 16 consecutive blocks per step (16-byte loads); the block
+// metadata (8 bytes per block) is re-read per pass from the cache.
 #include <climits>
 
 #include "pa_internal.h"
@@ -30,20 +31,51 @@ namespace {
 
 constexpr int kEvictThreads = 1024;
 constexpr int kWaves = kEvictThreads / 64;
+constexpr int kPerThread = 16;                          // consecutive blocks per thread and step
+constexpr int kPerStep = kEvictThreads * kPerThread;    // blocks per step
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int64_t block_key(int32_t ref, int32_t last, int32_t tick)
 {
     return 3 * ((int64_t)tick - last) - 7 * (int64_t)ref;
 }
 
-// Exclusive prefix count of `flag` over the workgroup (thread order) and the
+// The metadata of this thread's kPerThread blocks starting at `first`;
+// blocks past the pool read as free (refcount 0).
+__device__ __forceinline__ void load_blocks(const EvictArgs& a, int64_t first, int32_t (&ref)[kPerThread],
+                                            int32_t (&last)[kPerThread])
+{
+    if (first + kPerThread <= a.num_blocks) {
+#pragma unroll
+        for (int c = 0; c < kPerThread / 4; ++c) {
+            const i32x4 r = *reinterpret_cast<const i32x4*>(a.refcount + first + 4 * c);
+            const i32x4 l = *reinterpret_cast<const i32x4*>(a.last_used + first + 4 * c);
+            ref[4 * c] = r.x, ref[4 * c + 1] = r.y, ref[4 * c + 2] = r.z, ref[4 * c + 3] = r.w;
+            last[4 * c] = l.x, last[4 * c + 1] = l.y, last[4 * c + 2] = l.z, last[4 * c + 3] = l.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const bool in = first + i < a.num_blocks;
+            ref[i] = in ? a.refcount[first + i] : 0;
+            last[i] = in ? a.last_used[first + i] : 0;
+        }
+    }
+}
+
+// Exclusive prefix sum of `x` over the workgroup (thread order) and the
 // workgroup's total. `part` holds kWaves ints of LDS.
-__device__ __forceinline__ int block_prefix(bool flag, int* part, int& total)
+__device__ __forceinline__ int block_prefix(int x, int* part, int& total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint64_t m = __ballot(flag);
-    const int before_in_wave = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) part[w] = __popcll(m);
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        incl += lane >= d ? y : 0;
+    }
+    if (lane == 63) part[w] = incl;
     __syncthreads();
     int before = 0;
     total = 0;
@@ -53,7 +85,7 @@ __device__ __forceinline__ int block_prefix(bool flag, int* part, int& total)
         total += c;
     }
     __syncthreads();  // part[] is reused by the next call
-    return before + before_in_wave;
+    return before + incl - x;
 }
 
 __global__ __launch_bounds__(kEvictThreads) void evict_kernel(EvictArgs a)
@@ -65,17 +97,21 @@ __global__ __launch_bounds__(kEvictThreads) void evict_kernel(EvictArgs a)
     __shared__ unsigned long long s_prefix;
     __shared__ long long s_remaining;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int32_t ref[kPerThread], last[kPerThread];
 
     // 1. range of the keys and number of candidates
     long long kmin = LLONG_MAX, kmax = LLONG_MIN;
     int cnt = 0;
-    for (int64_t b = t; b < a.num_blocks; b += kEvictThreads) {
-        const int32_t r = a.refcount[b];
-        if (r <= 0) continue;
-        const long long key = block_key(r, a.last_used[b], a.tick);
-        kmin = key < kmin ? key : kmin;
-        kmax = key > kmax ? key : kmax;
-        ++cnt;
+    for (int64_t base = 0; base < a.num_blocks; base += kPerStep) {
+        load_blocks(a, base + (int64_t)t * kPerThread, ref, last);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if (ref[i] <= 0) continue;
+            const long long key = block_key(ref[i], last[i], a.tick);
+            kmin = key < kmin ? key : kmin;
+            kmax = key > kmax ? key : kmax;
+            ++cnt;
+        }
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
@@ -113,21 +149,27 @@ __global__ __launch_bounds__(kEvictThreads) void evict_kernel(EvictArgs a)
             if (t < 256) hist[t] = 0;
             __syncthreads();
             const unsigned long long prefix = s_prefix;
-            for (int64_t b = t; b < a.num_blocks; b += kEvictThreads) {
-                const int32_t r = a.refcount[b];
-                if (r <= 0) continue;
-                const unsigned long long u = (unsigned long long)(block_key(r, a.last_used[b], a.tick) - kmin);
-                if (shift + 8 < 64 && (u >> (shift + 8)) != (prefix >> (shift + 8))) continue;
-                atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            for (int64_t base = 0; base < a.num_blocks; base += kPerStep) {
+                load_blocks(a, base + (int64_t)t * kPerThread, ref, last);
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) {
+                    if (ref[i] <= 0) continue;
+                    const unsigned long long u = (unsigned long long)(block_key(ref[i], last[i], a.tick) - kmin);
+                    if (shift + 8 < 64 && (u >> (shift + 8)) != (prefix >> (shift + 8))) continue;
+                    atomicAdd(&hist[(u >> shift) & 255u], 1u);
+                }
             }
             __syncthreads();
-            if (t == 0) {  // the digit holding the remaining-th largest
-                long long above = 0, rem = s_remaining;
-                int d = 255;
-                for (; d > 0; --d) {
-                    if (above + hist[d] >= rem) break;
-                    above += hist[d];
-                }
+            // the digit holding the remaining-th largest: thread j looks at
+            // digit 255 - j; an exclusive prefix sum over the threads counts
+            // the keys in larger digits
+            const int d = 255 - t;
+            const int h = t < 256 ? (int)hist[d] : 0;
+            int all;
+            const long long above = block_prefix(h, part, all);
+            const long long rem = s_remaining;
+            __syncthreads();  // everyone has read s_remaining
+            if (t < 256 && above < rem && rem <= above + h) {
                 s_remaining = rem - above;
                 s_prefix = prefix | ((unsigned long long)d << shift);
             }
@@ -137,26 +179,38 @@ __global__ __launch_bounds__(kEvictThreads) void evict_kernel(EvictArgs a)
     const unsigned long long thr = s_prefix;  // the keff-th largest u
     const long long take_equal = s_remaining;  // how many of u == thr are chosen
 
-    // 3. chosen ids in block order
+    // 3. chosen ids in block order: each thread holds kPerThread consecutive
+    // blocks; prefix sums of per-thread counts give each its rank among the
+    // keys equal to the threshold and its first output slot
     long long chosen = 0, equal_seen = 0;
-    for (int64_t base = 0; keff > 0 && base < a.num_blocks; base += kEvictThreads) {
-        const int64_t b = base + t;
-        bool gt = false, eq = false;
-        if (b < a.num_blocks) {
-            const int32_t r = a.refcount[b];
-            if (r > 0) {
-                const unsigned long long u = (unsigned long long)(block_key(r, a.last_used[b], a.tick) - kmin);
-                gt = u > thr;
-                eq = u == thr;
-            }
+    for (int64_t base = 0; keff > 0 && base < a.num_blocks; base += kPerStep) {
+        const int64_t first = base + (int64_t)t * kPerThread;
+        load_blocks(a, first, ref, last);
+        unsigned gt = 0, eq = 0;  // bit i: block first + i
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if (ref[i] <= 0) continue;
+            const unsigned long long u = (unsigned long long)(block_key(ref[i], last[i], a.tick) - kmin);
+            gt |= (u > thr ? 1u : 0u) << i;
+            eq |= (u == thr ? 1u : 0u) << i;
         }
         int n_eq;
-        const long long eq_rank = equal_seen + block_prefix(eq, part, n_eq);
-        const bool sel = gt || (eq && eq_rank < take_equal);
+        long long eq_rank = equal_seen + block_prefix(__popc(eq), part, n_eq);
+        unsigned sel = gt;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if (!((eq >> i) & 1u)) continue;
+            if (eq_rank < take_equal) sel |= 1u << i;
+            ++eq_rank;
+        }
         int n_sel;
-        const long long pos = chosen + block_prefix(sel, part, n_sel);
-        if (sel && pos < keff) a.out[pos] = (int32_t)b;  // pos < keff always; the guard keeps
-                                                       // a wrong threshold from writing out of bounds
+        long long pos = chosen + block_prefix(__popc(sel), part, n_sel);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            if (!((sel >> i) & 1u)) continue;
+            if (pos < keff) a.out[pos] = (int32_t)(first + i);  // pos < keff always; the guard keeps
+            ++pos;                                              // a wrong threshold in bounds
+        }
         equal_seen += n_eq;
         chosen += n_sel;
     }

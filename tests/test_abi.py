@@ -158,6 +158,7 @@ def test_int8_append_needs_scales():
         ((FAKE, FAKE, 16, 5, -1, FAKE), pa.PA_ERR_SHAPE),
         ((FAKE, FAKE, 2**31, 5, 3, FAKE), pa.PA_ERR_UNSUPPORTED),
         ((FAKE + 2, FAKE, 16, 5, 3, FAKE), pa.PA_ERR_UNSUPPORTED),
+        ((FAKE, FAKE + 4, 16, 5, 3, FAKE), pa.PA_ERR_UNSUPPORTED),
         ((FAKE, FAKE, 16, 5, 0, None), pa.PA_OK),  # k == 0: nothing launched
     ],
 )
