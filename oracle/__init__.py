@@ -55,6 +55,14 @@ def lib() -> C.CDLL:
         L.pa_ref_paged_decode_f16.restype = i32
         L.pa_ref_paged_decode_int8.argtypes = [p, p, p, p, p] + common
         L.pa_ref_paged_decode_int8.restype = i32
+        L.pa_ref_e4m3_to_float.argtypes = [C.c_uint8]
+        L.pa_ref_e4m3_to_float.restype = f32
+        L.pa_ref_float_to_e4m3.argtypes = [f32]
+        L.pa_ref_float_to_e4m3.restype = C.c_uint8
+        L.pa_ref_quantize_kv_fp8.argtypes = [p, p, p, p, i64, i64, i32, i32, i32]
+        L.pa_ref_quantize_kv_fp8.restype = i32
+        L.pa_ref_paged_decode_fp8.argtypes = [p, p, p, p, p] + common
+        L.pa_ref_paged_decode_fp8.restype = i32
         app = [p, p, i32, i32, i32, i32, i32, i64]
         L.pa_ref_append_kv_f16.argtypes = [p, p, p, p] + app
         L.pa_ref_append_kv_f16.restype = i32
@@ -131,6 +139,37 @@ def paged_decode_int8(q, k_codes, v_codes, k_scale, v_scale, block_tables, conte
     kc, vc = _c(k_codes, np.int8), _c(v_codes, np.int8)
     ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
     return _decode(lib().pa_ref_paged_decode_int8, q, (kc, vc, ks, vs), block_tables,
+                   context_lens, softmax_scale, kc.shape[0], seq_ids, want_weights)
+
+
+def e4m3_to_float(code: int) -> float:
+    return float(lib().pa_ref_e4m3_to_float(int(code)))
+
+
+def float_to_e4m3(y: float) -> int:
+    return int(lib().pa_ref_float_to_e4m3(float(y)))
+
+
+def quantize_kv_fp8(pool: np.ndarray, block_ids=None):
+    """FP8 (E4M3) quantization of an fp16 pool ``[NB][H][B][d]``; returns
+    (codes uint8, scales f32 [NB][H]). Unlisted blocks keep code 0, scale 0."""
+    x = _c(pool, np.float16)
+    nb, h, bs, d = x.shape
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros((nb, h), np.float32)
+    ids = None if block_ids is None else _c(block_ids, np.int32)
+    rc = lib().pa_ref_quantize_kv_fp8(_ptr(x.view(np.uint16)), _ptr(codes), _ptr(scales),
+                                      _ptr(ids), 0 if ids is None else ids.size, nb, h, bs, d)
+    if rc:
+        raise ValueError(f"oracle fp8 quantize failed ({rc})")
+    return codes, scales
+
+
+def paged_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens,
+                     softmax_scale, seq_ids=None, want_weights=False):
+    kc, vc = _c(k_codes, np.uint8), _c(v_codes, np.uint8)
+    ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    return _decode(lib().pa_ref_paged_decode_fp8, q, (kc, vc, ks, vs), block_tables,
                    context_lens, softmax_scale, kc.shape[0], seq_ids, want_weights)
 
 

@@ -134,6 +134,91 @@ int pa_ref_quantize_kv_int8(const uint16_t* x, int8_t* codes, float* scales,
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 (OCP E4M3) per-(block, head) quantization.                            */
+/* The monograph's section 5.1 quantizes K and V with symmetric scales to    */
+/* FP8 or INT8 (Q_K = round(K / S_K)) and keeps one scale per block; the FP8 */
+/* format is not named there, and the reading here is OCP 8-bit E4M3: sign, */
+/* 4 exponent bits (bias 7), 3 mantissa bits, no infinities, S.1111.111 NaN, */
+/* largest finite 448. Per (block, head) tile, like the INT8 quantizer:      */
+/*   amax  = max |x|;  scale = amax / 448      (fp32, IEEE division)          */
+/*   code  = E4M3(x / scale)                   (IEEE division, then the      */
+/*           nearest E4M3 value, ties to an even mantissa, beyond 448 kept   */
+/*           at 448)                                                          */
+/* scale 0 gives code 0. A code decodes to fp32 exactly.                     */
+
+/* E4M3 code -> value (exact in fp32). */
+float pa_ref_e4m3_to_float(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexpf((float)m, -9);          /* subnormal: m * 2^-9 */
+    else
+        v = ldexpf((float)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* fp32 -> E4M3, round to nearest (ties to even), saturating at +-448.
+ * The step between neighbouring E4M3 values at |y| is 2^(max(E, -6) - 3),
+ * E = floor(log2 |y|); |y| / step is exact, rint rounds it half to even. */
+uint8_t pa_ref_float_to_e4m3(float y)
+{
+    if (y != y) return 0x7F;
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    float a = fabsf(y);
+    if (a == 0.0f) return sign;
+    int E;
+    frexpf(a, &E); /* a = f 2^E, f in [0.5, 1): floor(log2 a) = E - 1 */
+    E -= 1;
+    if (E < -6) E = -6;
+    float steps = nearbyintf(ldexpf(a, 3 - E)); /* multiples of the step */
+    float q = ldexpf(steps, E - 3);
+    if (q > 448.0f) q = 448.0f;
+    /* encode q: subnormal below 2^-6 */
+    if (q < 0.015625f) return sign | (uint8_t)(int)ldexpf(q, 9);
+    int e2;
+    float f = frexpf(q, &e2); /* q = f 2^e2, f in [0.5, 1) */
+    int m = (int)ldexpf(f, 4) - 8; /* q = (1 + m/8) 2^(e2-1) */
+    return sign | (uint8_t)(((e2 - 1 + 7) << 3) | m);
+}
+
+int pa_ref_quantize_kv_fp8(const uint16_t* x, uint8_t* codes, float* scales,
+                           const int32_t* block_ids, int64_t num_ids, int64_t num_blocks,
+                           int num_kv_heads, int block_size, int head_dim)
+{
+    if (!x || !codes || !scales || num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 ||
+        head_dim <= 0)
+        return REF_ERR_ARG;
+    int64_t count = block_ids ? num_ids : num_blocks;
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t b = block_ids ? block_ids[i] : i;
+        if (b < 0 || b >= num_blocks) return REF_ERR_TABLE;
+    }
+    const int64_t tile = (int64_t)block_size * head_dim;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t b = block_ids ? block_ids[i] : i;
+        if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+        for (int h = 0; h < num_kv_heads; ++h) {
+            const int64_t base = (b * num_kv_heads + h) * tile;
+            float amax = 0.0f;
+            for (int64_t e = 0; e < tile; ++e) {
+                float a = fabsf(pa_ref_half_to_float(x[base + e]));
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 448.0f;
+            scales[b * num_kv_heads + h] = scale;
+            for (int64_t e = 0; e < tile; ++e)
+                codes[base + e] = scale != 0.0f ? pa_ref_float_to_e4m3(pa_ref_half_to_float(x[base + e]) / scale)
+                                                : 0;
+        }
+    }
+    return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Single-query attention for one (sequence, query head) over gathered rows. */
 /*   s_t = softmax_scale * sum_j q_j k_tj                                    */
 /*   m   = max_t s_t,  p_t = exp(s_t - m),  l = sum_t p_t                    */
@@ -196,8 +281,8 @@ static int check_args(const int32_t* block_tables, const int32_t* context_lens, 
  * (dequantized as float(code) * scale of that (block, head)). */
 static void gather(int s, int kvh, int n, const int32_t* block_tables, int max_blocks_per_seq,
                    int num_kv_heads, int block_size, int head_dim, const uint16_t* k16,
-                   const uint16_t* v16, const int8_t* k8, const int8_t* v8, const float* ks,
-                   const float* vs, float* K, float* V)
+                   const uint16_t* v16, const int8_t* k8, const int8_t* v8, const uint8_t* kf8,
+                   const uint8_t* vf8, const float* ks, const float* vs, float* K, float* V)
 {
     for (int t = 0; t < n; ++t) {
         int64_t b = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
@@ -207,6 +292,11 @@ static void gather(int s, int kvh, int n, const int32_t* block_tables, int max_b
             if (k16) {
                 K[(int64_t)t * head_dim + j] = pa_ref_half_to_float(k16[row + j]);
                 V[(int64_t)t * head_dim + j] = pa_ref_half_to_float(v16[row + j]);
+            } else if (kf8) {
+                float sk = ks[b * num_kv_heads + kvh];
+                float sv = vs[b * num_kv_heads + kvh];
+                K[(int64_t)t * head_dim + j] = pa_ref_e4m3_to_float(kf8[row + j]) * sk;
+                V[(int64_t)t * head_dim + j] = pa_ref_e4m3_to_float(vf8[row + j]) * sv;
             } else {
                 float sk = ks[b * num_kv_heads + kvh];
                 float sv = vs[b * num_kv_heads + kvh];
@@ -218,7 +308,8 @@ static void gather(int s, int kvh, int n, const int32_t* block_tables, int max_b
 }
 
 static int decode_common(const uint16_t* q, const uint16_t* k16, const uint16_t* v16,
-                         const int8_t* k8, const int8_t* v8, const float* ks, const float* vs,
+                         const int8_t* k8, const int8_t* v8, const uint8_t* kf8,
+                         const uint8_t* vf8, const float* ks, const float* vs,
                          const int32_t* block_tables, const int32_t* context_lens, float* out,
                          int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                          int block_size, int max_blocks_per_seq, int64_t num_blocks,
@@ -256,7 +347,7 @@ static int decode_common(const uint16_t* q, const uint16_t* k16, const uint16_t*
             const int64_t qrow = ((int64_t)s * num_q_heads + h) * head_dim;
             for (int j = 0; j < head_dim; ++j) qf[j] = pa_ref_half_to_float(q[qrow + j]);
             gather(s, kvh, n, block_tables, max_blocks_per_seq, num_kv_heads, block_size,
-                   head_dim, k16, v16, k8, v8, ks, vs, K, V);
+                   head_dim, k16, v16, k8, v8, kf8, vf8, ks, vs, K, V);
             float* w = weights ? weights + ((int64_t)s * num_q_heads + h) * weights_stride : NULL;
             attend(qf, K, V, n, head_dim, softmax_scale, out + qrow, w, sc);
         }
@@ -280,7 +371,7 @@ int pa_ref_paged_decode_f16(const uint16_t* q, const uint16_t* k_pool, const uin
                             float* weights, int weights_stride)
 {
     if (!k_pool || !v_pool) return REF_ERR_ARG;
-    return decode_common(q, k_pool, v_pool, NULL, NULL, NULL, NULL, block_tables, context_lens,
+    return decode_common(q, k_pool, v_pool, NULL, NULL, NULL, NULL, NULL, NULL, block_tables, context_lens,
                          out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, softmax_scale, seq_ids, num_seq_ids,
                          weights, weights_stride);
@@ -298,10 +389,28 @@ int pa_ref_paged_decode_int8(const uint16_t* q, const int8_t* k_codes, const int
                              float* weights, int weights_stride)
 {
     if (!k_codes || !v_codes || !k_scale || !v_scale) return REF_ERR_ARG;
-    return decode_common(q, NULL, NULL, k_codes, v_codes, k_scale, v_scale, block_tables,
+    return decode_common(q, NULL, NULL, k_codes, v_codes, NULL, NULL, k_scale, v_scale, block_tables,
                          context_lens, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
                          block_size, max_blocks_per_seq, num_blocks, softmax_scale, seq_ids,
                          num_seq_ids, weights, weights_stride);
+}
+
+/* FP8 KV: E4M3 codes [NB][H_kv][B][d] with scales [NB][H_kv] fp32 for K and
+ * for V; every element is decoded exactly and multiplied by its scale (one
+ * fp32 multiply), then the same attention runs. */
+int pa_ref_paged_decode_fp8(const uint16_t* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, const int32_t* context_lens, float* out,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int64_t num_blocks,
+                            float softmax_scale, const int32_t* seq_ids, int num_seq_ids,
+                            float* weights, int weights_stride)
+{
+    if (!k_codes || !v_codes || !k_scale || !v_scale) return REF_ERR_ARG;
+    return decode_common(q, NULL, NULL, NULL, NULL, k_codes, v_codes, k_scale, v_scale,
+                         block_tables, context_lens, out, num_seqs, num_q_heads, num_kv_heads,
+                         head_dim, block_size, max_blocks_per_seq, num_blocks, softmax_scale,
+                         seq_ids, num_seq_ids, weights, weights_stride);
 }
 
 /* ------------------------------------------------------------------------ */
