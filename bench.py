@@ -119,7 +119,7 @@ def main() -> int:
     ws16 = pa.workspace_for(q, k16, tables, args.partition_tokens)
     ws8 = pa.workspace_for(q, k8, tables, args.partition_tokens)
     shares = {name: pa.pa_decode_shares(w.num_seqs, w.num_kv_heads, w.head_dim, w.max_blocks_per_seq,
-                                        16, args.partition_tokens, kv_int8=i8)
+                                        16, args.partition_tokens, kv_format=pa.KV_INT8 if i8 else pa.KV_F16)
               for name, i8 in (("fp16", False), ("int8", True))}
     torch.cuda.synchronize()
 

@@ -80,6 +80,19 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
                         int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
                         int head_dim, void* stream);
 
+/* The FP8 variant of pa_quantize_kv_int8 (monograph section 5.1: FP8 or INT8
+ * codes with symmetric per-block scales; the format read as OCP 8-bit E4M3:
+ * bias 7, largest finite 448, no infinities). Per (block, KV head) tile:
+ *     amax = max |x|,  scale = amax / 448 (fp32, IEEE-rounded division),
+ *     code = the E4M3 value nearest to x / scale (an IEEE fp32 division; ties
+ *     to an even mantissa), and scale 0 gives codes 0.
+ *  k_fp8, v_fp8   out: E4M3 code pools (bytes) [num_blocks][num_kv_heads][16][head_dim]
+ * Other arguments, layouts and errors as pa_quantize_kv_int8. */
+int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uint8_t* v_fp8,
+                       float* k_scale, float* v_scale, const int32_t* block_ids,
+                       int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                       int head_dim, void* stream);
+
 /* Work split of the decode calls. For every KV head the tiles of all
  * sequences, in sequence order, are cut into equal contiguous shares, one
  * 64-lane wave each; a (sequence, KV head) whose tiles fall in one share is
@@ -88,7 +101,8 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
  * partition_tokens: the wanted tokens per share for the longest possible
  * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
  * to let the library size one share per wave the current device holds at
- * once. kv_int8: 0 for pa_paged_decode_f16, nonzero for pa_paged_decode_int8.
+ * once. kv_format: 0 for pa_paged_decode_f16, 1 for pa_paged_decode_int8, 2
+ * for pa_paged_decode_fp8 (other values are rejected).
  *
  * pa_decode_shares returns the number of shares per KV head, or a negative
  * PA_ERR_* code for arguments the decode calls would reject.
@@ -97,10 +111,10 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
  * for arguments the decode calls would reject. Both depend on the current
  * device's compute-unit count when partition_tokens is 0. */
 int pa_decode_shares(int num_seqs, int num_kv_heads, int head_dim, int max_blocks_per_seq,
-                     int block_size, int partition_tokens, int kv_int8);
+                     int block_size, int partition_tokens, int kv_format);
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_blocks_per_seq, int block_size, int partition_tokens,
-                                 int kv_int8);
+                                 int kv_format);
 
 /* Decode attention over an fp16 paged KV cache. For every sequence s and
  * query head h, with n = context_lens[s] and k_t, v_t the K/V rows of token t
@@ -134,6 +148,18 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          int block_size, int max_blocks_per_seq, int64_t num_blocks,
                          float softmax_scale, int partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Same as pa_paged_decode_int8 over an FP8 (OCP E4M3) cache produced by
+ * pa_quantize_kv_fp8: K and V elements are e4m3(code) * scale of their
+ * (block, KV head) (monograph section 5.1's FP8 variant).
+ *  k_cache, v_cache: E4M3 codes (bytes) [num_blocks][num_kv_heads][16][head_dim]
+ *  k_scale, v_scale: fp32 [num_blocks][num_kv_heads] */
+int pa_paged_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float* out, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                        int64_t num_blocks, float softmax_scale, int partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Choose the physical blocks to evict (PagedKV-Fusion README, "Overview",
  * component A: scoring plus a top-k over the paged blocks, the "bottom-k

@@ -35,10 +35,12 @@ PA_ERR_HIP = -5
 EXPORTED = (
     "pa_error_string",
     "pa_quantize_kv_int8",
+    "pa_quantize_kv_fp8",
     "pa_decode_workspace_bytes",
     "pa_decode_shares",
     "pa_paged_decode_f16",
     "pa_paged_decode_int8",
+    "pa_paged_decode_fp8",
     "pa_append_kv_f16",
     "pa_append_kv_int8",
     "pa_evict_select",
@@ -67,6 +69,8 @@ def lib() -> C.CDLL:
         L.pa_error_string.restype = C.c_char_p
         L.pa_quantize_kv_int8.argtypes = [p, p, p, p, p, p, p, i64, i64, i32, i32, i32, p]
         L.pa_quantize_kv_int8.restype = i32
+        L.pa_quantize_kv_fp8.argtypes = [p, p, p, p, p, p, p, i64, i64, i32, i32, i32, p]
+        L.pa_quantize_kv_fp8.restype = i32
         L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.pa_decode_workspace_bytes.restype = sz
         L.pa_decode_shares.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -76,6 +80,8 @@ def lib() -> C.CDLL:
         L.pa_paged_decode_f16.restype = i32
         L.pa_paged_decode_int8.argtypes = [p, p, p, p, p] + tail
         L.pa_paged_decode_int8.restype = i32
+        L.pa_paged_decode_fp8.argtypes = [p, p, p, p, p] + tail
+        L.pa_paged_decode_fp8.restype = i32
         app = [p, p, i32, i32, i32, i32, i32, i64, p]
         L.pa_append_kv_f16.argtypes = [p, p, p, p] + app
         L.pa_append_kv_f16.restype = i32
@@ -112,6 +118,56 @@ def _need(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+KV_F16, KV_INT8, KV_FP8 = 0, 1, 2
+
+
+def kv_format_of(cache) -> int:
+    """The cache format of a K/V pool tensor: fp16, int8 codes, or E4M3 codes
+    (torch.uint8 or torch.float8_e4m3fn)."""
+    import torch
+
+    if cache.dtype == torch.float16:
+        return KV_F16
+    if cache.dtype == torch.int8:
+        return KV_INT8
+    if cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        return KV_FP8
+    raise TypeError(f"no KV cache format for {cache.dtype}")
+
+
+def _need_fp8(t, name, ndim):
+    import torch
+
+    if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise TypeError(f"{name} must be torch.uint8 or torch.float8_e4m3fn, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pa_quantize_kv_fp8(k_f16, v_f16, k_fp8, v_fp8, k_scale, v_scale, block_ids=None, stream=None):
+    """Quantize fp16 K/V pools to FP8 (OCP E4M3) codes plus one fp32 scale per (block, head)."""
+    import torch
+
+    for t, n in ((k_f16, "k_f16"), (v_f16, "v_f16")):
+        _need(t, n, torch.float16, 4)
+    for t, n in ((k_fp8, "k_fp8"), (v_fp8, "v_fp8")):
+        _need_fp8(t, n, 4)
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, n, torch.float32, 2)
+    nb, hkv, bs, d = k_f16.shape
+    nids = 0
+    if block_ids is not None:
+        _need(block_ids, "block_ids", torch.int32, 1)
+        nids = block_ids.numel()
+    rc = lib().pa_quantize_kv_fp8(_ptr(k_f16), _ptr(v_f16), _ptr(k_fp8), _ptr(v_fp8),
+                                  _ptr(k_scale), _ptr(v_scale), _ptr(block_ids), nids, nb, hkv,
+                                  bs, d, _stream(k_f16, stream))
+    if rc:
+        raise PagedAttentionError("pa_quantize_kv_fp8", rc)
+
+
 def pa_quantize_kv_int8(k_f16, v_f16, k_i8, v_i8, k_scale, v_scale, block_ids=None, stream=None):
     """Quantize fp16 K/V pools to INT8 codes plus one fp32 scale per (block, head)."""
     import torch
@@ -135,16 +191,16 @@ def pa_quantize_kv_int8(k_f16, v_f16, k_i8, v_i8, k_scale, v_scale, block_ids=No
 
 
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                              block_size=16, partition_tokens=0, kv_int8=False) -> int:
+                              block_size=16, partition_tokens=0, kv_format=KV_F16) -> int:
     return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                max_blocks_per_seq, block_size, partition_tokens,
-                                               int(bool(kv_int8))))
+                                               int(kv_format)))
 
 
 def pa_decode_shares(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, block_size=16,
-                     partition_tokens=0, kv_int8=False) -> int:
+                     partition_tokens=0, kv_format=KV_F16) -> int:
     r = int(lib().pa_decode_shares(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
-                                   block_size, partition_tokens, int(bool(kv_int8))))
+                                   block_size, partition_tokens, int(kv_format)))
     if r < 0:
         raise PagedAttentionError("pa_decode_shares", r)
     return r
@@ -157,7 +213,7 @@ def workspace_for(q, k_cache, block_tables, partition_tokens=0):
 
     n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], k_cache.shape[1], q.shape[2],
                                   block_tables.shape[1], k_cache.shape[2], partition_tokens,
-                                  k_cache.dtype == torch.int8)
+                                  kv_format_of(k_cache))
     return torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
 
 
@@ -291,9 +347,32 @@ def pa_evict_select(refcount, last_used, current_tick, k, out_ids=None, stream=N
     return out_ids
 
 
+def pa_paged_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                        softmax_scale, partition_tokens=0, workspace=None, stream=None):
+    """Decode attention over an FP8 (OCP E4M3) paged cache with per-(block, head) scales."""
+    import torch
+
+    _need_fp8(k_cache, "k_cache", 4)
+    _need_fp8(v_cache, "v_cache", 4)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    _need(v_scale, "v_scale", torch.float32, 2)
+    S, hq, hkv, d, bs, mb, nb = _decode_args(q, k_cache, block_tables, context_lens, out)
+    if workspace is None:
+        workspace = workspace_for(q, k_cache, block_tables, partition_tokens)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().pa_paged_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                   _ptr(out), S, hq, hkv, d, bs, mb, nb, float(softmax_scale),
+                                   int(partition_tokens), _ptr(workspace), wbytes,
+                                   _stream(q, stream))
+    if rc:
+        raise PagedAttentionError("pa_paged_decode_fp8", rc)
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
-    "pa_append_kv_int8", "pa_evict_select",
+    "pa_append_kv_int8", "pa_evict_select", "pa_quantize_kv_fp8", "pa_paged_decode_fp8",
+    "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8",
 ]

@@ -39,7 +39,7 @@ int num_compute_units()
 // heads, and no share shorter than 8 blocks of that bound. Never more shares
 // than the bound has blocks.
 long long shares_per_head(int num_seqs, int num_kv_heads, int head_dim, int max_blocks,
-                          int partition_tokens, bool int8)
+                          int partition_tokens, int fmt)
 {
     const long long bound = (long long)num_seqs * max_blocks;
     if (bound <= 0) return 1;
@@ -47,7 +47,7 @@ long long shares_per_head(int num_seqs, int num_kv_heads, int head_dim, int max_
     if (partition_tokens > 0) {
         k = (bound * pa::kBlockTokens + partition_tokens - 1) / partition_tokens;
     } else {
-        const long long waves = (long long)num_compute_units() * pa::decode_waves_per_cu(head_dim, int8);
+        const long long waves = (long long)num_compute_units() * pa::decode_waves_per_cu(head_dim, fmt);
         k = std::max(1LL, waves / num_kv_heads);
         k = std::min(k, (bound + 7) / 8);
     }
@@ -71,11 +71,10 @@ int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head
     if ((long long)max_blocks_per_seq * pa::kBlockTokens > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     // tile prefix sums are int32; one workgroup per (share, KV head)
     if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    if (shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, false) *
-                num_kv_heads > 0x7fffffffLL ||
-        shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, true) *
+    for (int fmt = pa::kKvF16; fmt <= pa::kKvF8; ++fmt)
+        if (shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, fmt) *
                 num_kv_heads > 0x7fffffffLL)
-        return PA_ERR_UNSUPPORTED;
+            return PA_ERR_UNSUPPORTED;
     return PA_OK;
 }
 
@@ -84,10 +83,10 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
                   int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                   int max_blocks_per_seq, int64_t num_blocks, float softmax_scale,
                   int partition_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                  bool int8)
+                  int fmt)
 {
     if (!q || !k || !v || !tables || !ctx || !out) return PA_ERR_NULL;
-    if (int8 && (!ks || !vs)) return PA_ERR_NULL;
+    if (fmt != pa::kKvF16 && (!ks || !vs)) return PA_ERR_NULL;
     int rc = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, num_blocks, partition_tokens);
     if (rc) return rc;
@@ -97,7 +96,7 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     if (num_seqs == 0) return PA_OK;
 
     const int shares = (int)shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
-                                            partition_tokens, int8);
+                                            partition_tokens, fmt);
     const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, head_dim, shares);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
@@ -121,7 +120,7 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     a.max_blocks = max_blocks_per_seq;
     a.shares = shares;
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-    hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, int8,
+    hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, fmt,
                                      static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }
@@ -159,6 +158,36 @@ int append_common(const void* k_new, const void* v_new, void* k_cache, void* v_c
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
+int quantize_common(const void* k_f16, const void* v_f16, void* k_i8, void* v_i8, float* k_scale,
+                    float* v_scale, const int32_t* block_ids, int64_t num_ids, int64_t num_blocks,
+                    int num_kv_heads, int block_size, int head_dim, void* stream, bool fp8)
+{
+    if (!k_f16 || !v_f16 || !k_i8 || !v_i8 || !k_scale || !v_scale) return PA_ERR_NULL;
+    if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
+        return PA_ERR_SHAPE;
+    if (block_ids && num_ids < 0) return PA_ERR_SHAPE;
+    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (!aligned16(k_f16) || !aligned16(v_f16) || (reinterpret_cast<uintptr_t>(k_i8) & 7u) ||
+        (reinterpret_cast<uintptr_t>(v_i8) & 7u))
+        return PA_ERR_UNSUPPORTED;
+    pa::QuantArgs a;
+    a.k = static_cast<const uint16_t*>(k_f16);
+    a.v = static_cast<const uint16_t*>(v_f16);
+    a.kc = static_cast<int8_t*>(k_i8);
+    a.vc = static_cast<int8_t*>(v_i8);
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.ids = block_ids;
+    a.num_ids = block_ids ? num_ids : num_blocks;
+    a.num_blocks = num_blocks;
+    a.num_kv_heads = num_kv_heads;
+    if ((a.num_ids * num_kv_heads * 2 + 3) / 4 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    hipError_t e = fp8 ? pa::launch_quantize_fp8(a, head_dim, static_cast<hipStream_t>(stream))
+                       : pa::launch_quantize(a, head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,54 +212,44 @@ int pa_quantize_kv_int8(const void* k_f16, const void* v_f16, int8_t* k_i8, int8
                         int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
                         int head_dim, void* stream)
 {
-    if (!k_f16 || !v_f16 || !k_i8 || !v_i8 || !k_scale || !v_scale) return PA_ERR_NULL;
-    if (num_blocks <= 0 || num_kv_heads <= 0 || block_size <= 0 || head_dim <= 0)
-        return PA_ERR_SHAPE;
-    if (block_ids && num_ids < 0) return PA_ERR_SHAPE;
-    if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
-    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (!aligned16(k_f16) || !aligned16(v_f16) || (reinterpret_cast<uintptr_t>(k_i8) & 7u) ||
-        (reinterpret_cast<uintptr_t>(v_i8) & 7u))
-        return PA_ERR_UNSUPPORTED;
-    pa::QuantArgs a;
-    a.k = static_cast<const uint16_t*>(k_f16);
-    a.v = static_cast<const uint16_t*>(v_f16);
-    a.kc = k_i8;
-    a.vc = v_i8;
-    a.ks = k_scale;
-    a.vs = v_scale;
-    a.ids = block_ids;
-    a.num_ids = block_ids ? num_ids : num_blocks;
-    a.num_blocks = num_blocks;
-    a.num_kv_heads = num_kv_heads;
-    if ((a.num_ids * num_kv_heads * 2 + 3) / 4 > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    hipError_t e = pa::launch_quantize(a, head_dim, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? PA_OK : hip_fail(e);
+    return quantize_common(k_f16, v_f16, k_i8, v_i8, k_scale, v_scale, block_ids, num_ids,
+                           num_blocks, num_kv_heads, block_size, head_dim, stream, false);
+}
+
+int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uint8_t* v_fp8,
+                       float* k_scale, float* v_scale, const int32_t* block_ids,
+                       int64_t num_ids, int64_t num_blocks, int num_kv_heads, int block_size,
+                       int head_dim, void* stream)
+{
+    return quantize_common(k_f16, v_f16, k_fp8, v_fp8, k_scale, v_scale, block_ids, num_ids,
+                           num_blocks, num_kv_heads, block_size, head_dim, stream, true);
 }
 
 int pa_decode_shares(int num_seqs, int num_kv_heads, int head_dim, int max_blocks_per_seq,
-                     int block_size, int partition_tokens, int kv_int8)
+                     int block_size, int partition_tokens, int kv_format)
 {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
         partition_tokens < 0 || partition_tokens % pa::kBlockTokens)
         return PA_ERR_SHAPE;
     if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (kv_format < pa::kKvF16 || kv_format > pa::kKvF8) return PA_ERR_UNSUPPORTED;
     if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
     return (int)std::min(shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
-                                         partition_tokens, kv_int8 != 0),
+                                         partition_tokens, kv_format),
                          0x7fffffffLL);
 }
 
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                  int max_blocks_per_seq, int block_size, int partition_tokens,
-                                 int kv_int8)
+                                 int kv_format)
 {
+    if (kv_format < pa::kKvF16 || kv_format > pa::kKvF8) return 0;
     if (check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                            max_blocks_per_seq, 1, partition_tokens))
         return 0;
     const long long shares = shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
-                                             partition_tokens, kv_int8 != 0);
+                                             partition_tokens, kv_format);
     return pa::workspace_bytes(num_seqs, num_q_heads, head_dim, (int)shares);
 }
 
@@ -244,7 +263,7 @@ int pa_paged_decode_f16(const void* q, const void* k_cache, const void* v_cache,
     return decode_common(q, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens, out,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
-                         workspace, workspace_bytes, stream, false);
+                         workspace, workspace_bytes, stream, pa::kKvF16);
 }
 
 int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_cache,
@@ -258,7 +277,20 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
     return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
-                         workspace, workspace_bytes, stream, true);
+                         workspace, workspace_bytes, stream, pa::kKvI8);
+}
+
+int pa_paged_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float* out, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                        int64_t num_blocks, float softmax_scale, int partition_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
+                         workspace, workspace_bytes, stream, pa::kKvF8);
 }
 
 int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t num_blocks,

@@ -145,13 +145,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st)
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)
 {
     const int zero_groups = a.num_seqs < 256 ? a.num_seqs : 256;
     hipLaunchKernelGGL(decode_prep_kernel, dim3(1 + zero_groups), dim3(kPrepThreads), 0, st, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_decode_waves(a, head_dim, group, int8, st);
+    e = launch_decode_waves(a, head_dim, group, fmt, st);
     if (e != hipSuccess) return e;
     const dim3 grid(a.num_q_heads, a.num_seqs);
     if (head_dim == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, st, a, group);

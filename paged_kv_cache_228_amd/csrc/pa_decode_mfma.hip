@@ -8,11 +8,17 @@
 // section 5.2 for softmax(Q K^T / sqrt d) V): for sequence s and query head
 // h, out = sum_t softmax_t(scale * q.k_t) v_t over the sequence's tokens.
 //
-// Work decomposition: one wave (the whole workgroup) per (sequence, KV head,
-// context partition). The wave stages the partition's block ids (and, for
-// INT8, the tiles' scales) in LDS and streams the partition's (block, head)
-// tiles in slots of SLOT consecutive blocks through a two-slot register ring:
-// one slot's loads are in flight while the other slot is computed.
+// Work decomposition: one wave (the whole workgroup) per (share, KV head):
+// a share is a contiguous range of the head's tiles over all sequences
+// (pa_split.h). The wave stages a chunk of block ids in LDS and streams the
+// (block, head) tiles in slots of SLOT consecutive blocks through a two-slot
+// register ring: one slot's loads are in flight while the other is computed.
+//
+// Three cache formats, one kernel template (F): fp16; INT8 codes with one
+// fp32 scale per (block, head) for K and for V; FP8 (OCP E4M3) codes with
+// the same scales (monograph section 5.1's FP8 variant). INT8 scores run on
+// the int8 matrix cores; FP8 tiles are widened to fp16 in registers and take
+// the fp16 path.
 //
 // Per 16-token tile, with the G <= 8 query heads of the KV head in the 16
 // columns of the MFMA tile:
@@ -26,14 +32,17 @@
 // lanes. Columns 0..7 of Q^T hold the group's heads and columns 8..15 the
 // same heads again, so rows h and h + 8 of P carry the fp16 hi and lo halves
 // of head h's weights (about 20 significant bits together) and one product
-// covers both; the two output rows are added once at the end. K and V enter
-// as fp16 (INT8 codes convert to fp16 exactly). Accumulation is fp32.
+// covers both; the two output rows are added once at the end. V enters as
+// fp16 (INT8 and E4M3 codes convert to fp16 exactly), K as fp16 or, for INT8,
+// as raw codes. Accumulation is fp32.
 //
 // Online softmax with a lazy reference: scores are kept in the log2 domain;
 // the running reference max m of each head is only raised when a slot holds a
 // score more than kLazy above it, so p = 2^(s - m) <= 2^kLazy and the rescale
 // of the accumulators is rare. The result is the same softmax: every partial
 // sum carries the same reference, and the merge divides it out.
+#include <type_traits>
+
 #include "pa_internal.h"
 #include "pa_split.h"
 
@@ -61,6 +70,9 @@ constexpr float kPUnscale = 1.0f / 64.0f;
 #ifndef PA_SLOT_I8
 #define PA_SLOT_I8 2
 #endif
+#ifndef PA_SLOT_F8
+#define PA_SLOT_F8 2
+#endif
 // Cache-policy bits of the K/V tile loads (2: non-temporal).
 #ifndef PA_KV_AUX
 #define PA_KV_AUX 2
@@ -74,6 +86,9 @@ constexpr float kPUnscale = 1.0f / 64.0f;
 #endif
 #ifndef PA_MINW_I8
 #define PA_MINW_I8 2
+#endif
+#ifndef PA_MINW_F8
+#define PA_MINW_F8 2
 #endif
 
 // Element i of a 4-dword vector (i a compile-time constant after unrolling).
@@ -132,15 +147,46 @@ __device__ __forceinline__ uint32_t half_pair(uint32_t w0, uint32_t w1, int h)
     return __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u);
 }
 
-template <int D, bool I8>
+// E4M3 -> fp16 for two codes that sit in bits 8..15 and 24..31 of x: the
+// code's sign goes to the fp16 sign and its 7 exponent-and-mantissa bits to
+// fp16 bits 7..13, which makes the fp16 value exactly the code's value times
+// 2^-8 (E4M3 subnormals land on fp16 subnormals, the bias differs by 8). The
+// 2^8 is folded into the tile's scales.
+__device__ __forceinline__ uint32_t e4m3_hi_bytes_to_half2(uint32_t x)
+{
+    return (x & 0x80008000u) | ((x >> 1) & 0x3F803F80u);
+}
+
+// Codes b, b+1 of word w as an fp16 pair (x 2^-8).
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, int b)
+{
+    const uint32_t sel = 0x0Cu | ((uint32_t)b << 8) | (0x0Cu << 16) | ((uint32_t)(b + 1) << 24);
+    return e4m3_hi_bytes_to_half2(__builtin_amdgcn_perm(w, w, sel));
+}
+
+// Code b of words w0 and w1 as an fp16 pair (x 2^-8).
+__device__ __forceinline__ uint32_t e4m3_pair2(uint32_t w0, uint32_t w1, int b)
+{
+    const uint32_t sel = 0x0Cu | ((uint32_t)b << 8) | (0x0Cu << 16) | ((uint32_t)(4 + b) << 24);
+    return e4m3_hi_bytes_to_half2(__builtin_amdgcn_perm(w1, w0, sel));
+}
+
+template <int D, int F>
 struct MCfg {
-    static constexpr int EB = I8 ? 1 : 2;      // bytes per element
-    static constexpr int ROW = D * EB;         // bytes per token row of a tile
-    static constexpr int TILE = 16 * ROW;      // bytes per (block, head) tile
+    static constexpr bool I8 = F == kKvI8;     // int8 codes on the int8 matrix cores
+    static constexpr bool SCALED = F != kKvF16;  // per-(block, head) K and V scales
+    static constexpr int EB = I8 ? 1 : 2;      // bytes per element in registers and LDS
+    static constexpr int SEB = F == kKvF16 ? 2 : 1;  // bytes per element in the pool
+    static constexpr int ROW = D * EB;         // bytes per token row of a register tile
+    static constexpr int TILE = 16 * ROW;      // bytes per register tile
+    static constexpr int STILE = 16 * D * SEB; // bytes per (block, head) tile in the pool
     static constexpr int NQK = D / 32;         // 16x16x32 MFMAs for Q.K^T per tile
-    static constexpr int KLD = I8 ? (NQK + 1) / 2 : NQK;  // 16-byte K loads per lane
+    static constexpr int KLD = I8 ? (NQK + 1) / 2 : NQK;  // 16-byte K registers per lane
     static constexpr int DPL = D / 16;         // V dims per lane
-    static constexpr int VB = DPL * EB;        // V bytes per lane per token
+    static constexpr int VB = DPL * EB;        // V register bytes per lane per token
+    static constexpr int SVB = DPL * SEB;      // V pool bytes per lane per token
+    // the E4M3 -> fp16 widening leaves values x 2^-8; the scales take the 2^8
+    static constexpr float SCALE_FIX = F == kKvF8 ? 256.0f : 1.0f;
 };
 
 template <int VB> struct VChunk;
@@ -156,40 +202,48 @@ __device__ __forceinline__ typename VChunk<VB>::type vload(rsrc_t r, int off)
     else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, PA_KV_AUX);
 }
 
-template <int D, bool I8>
+// A tile as loaded: K in tile order (FP8: 8 codes per register pair), V as
+// four token rows of this lane's dims, both in the pool's element size.
+template <int D, int F>
 struct MTile {
-    using C = MCfg<D, I8>;
-    u32x4 k[C::KLD];
-    typename VChunk<C::VB>::type v[4];
+    using C = MCfg<D, F>;
+    typename std::conditional<F == kKvF8, u32x2, u32x4>::type k[C::KLD];
+    typename VChunk<C::SVB>::type v[4];
 };
 
 // Issue every load of one tile (and, for INT8, of its K and V scales).
 // valid == false (past the chunk) or bid < 0 (an id outside the pool, marked
 // when staged) gives a zero-byte descriptor: the loads return zeros and touch
 // no memory, and the scales are 0.
-template <int D, bool I8>
-__device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, int bid, bool valid,
+template <int D, int F>
+__device__ __forceinline__ void mload(MTile<D, F>& t, const DecodeArgs& a, int bid, bool valid,
                                       int kvh, int lane, float& ksc, float& vsc)
 {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     const bool in_pool = valid && bid >= 0;
     const int64_t b = in_pool ? bid : 0;
-    if constexpr (I8) {  // uniform addresses: one scalar load each
+    if constexpr (C::SCALED) {  // uniform addresses: one scalar load each
         const int64_t si = b * a.num_kv_heads + kvh;
-        ksc = in_pool ? a.k_scale[si] : 0.0f;
-        vsc = in_pool ? a.v_scale[si] : 0.0f;
+        ksc = in_pool ? a.k_scale[si] * C::SCALE_FIX : 0.0f;
+        vsc = in_pool ? a.v_scale[si] * C::SCALE_FIX : 0.0f;
     }
-    const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::TILE;
-    const int bytes = in_pool ? C::TILE : 0;
+    const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::STILE;
+    const int bytes = in_pool ? C::STILE : 0;
     const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
     const rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + off, bytes);
     const int g = lane >> 4, n = lane & 15;
     // K in the tile's own order: instruction c reads bytes [1024c, 1024c + 1024)
+    // (FP8: [512c, 512c + 512), the codes of the fp16 layout's elements)
 #pragma unroll
-    for (int c = 0; c < C::KLD; ++c) t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * c + 16 * lane, 0, PA_KV_AUX);
+    for (int c = 0; c < C::KLD; ++c) {
+        if constexpr (F == kKvF8)
+            t.k[c] = __builtin_amdgcn_raw_buffer_load_b64(rk, 512 * c + 8 * lane, 0, PA_KV_AUX);
+        else
+            t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * c + 16 * lane, 0, PA_KV_AUX);
+    }
     // V: token 4g+ks, this lane's DPL dims (n * DPL ..)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) t.v[ks] = vload<C::VB>(rv, (4 * g + ks) * C::ROW + n * C::VB);
+    for (int ks = 0; ks < 4; ++ks) t.v[ks] = vload<C::SVB>(rv, (4 * g + ks) * D * C::SEB + n * C::SVB);
 }
 
 // K reaches the matrix cores through LDS. A load in operand order (lane =
@@ -201,9 +255,9 @@ __device__ __forceinline__ void mload(MTile<D, I8>& t, const DecodeArgs& a, int 
 // swizzle for which both the in-order writes and the operand-order reads hit
 // distinct LDS banks (whether the hardware serves 8 lanes per 128 bytes or
 // 16 lanes per 256 bytes per pass).
-template <int D, bool I8>
+template <int D, int F>
 struct KSwz {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     static_assert(C::ROW == 256 || C::ROW == 128 || C::ROW == 64, "row of 64, 128 or 256 bytes");
     static constexpr int KREG = C::TILE / 1024;  // 16-byte registers per lane per tile
     __device__ static int f(int r)
@@ -219,12 +273,12 @@ struct KSwz {
 // Rearrange the K registers of one tile from tile order to operand order
 // through the wave's LDS tile `kl`: afterwards k[c] holds, for lane (g, n),
 // token n's 16-byte chunk 4c+g (fp16) or g+4c (INT8).
-template <int D, bool I8, int KL>
+template <int D, int F, int KL>
 __device__ __forceinline__ void k_to_operand(u32x4 (&k)[KL], u32x4* kl, int lane)
 {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     static_assert(KL == C::KLD, "K registers of one tile");
-    using S = KSwz<D, I8>;
+    using S = KSwz<D, F>;
     static_assert(S::KREG == C::KLD, "one 16-byte register per 1024 bytes of K");
     const int g = lane >> 4, n = lane & 15;
 #pragma unroll
@@ -234,17 +288,17 @@ __device__ __forceinline__ void k_to_operand(u32x4 (&k)[KL], u32x4* kl, int lane
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int c = 0; c < C::KLD; ++c) k[c] = kl[S::at(n, I8 ? (g + 4 * c) : (4 * c + g))];
+    for (int c = 0; c < C::KLD; ++c) k[c] = kl[S::at(n, C::I8 ? (g + 4 * c) : (4 * c + g))];
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, bool I8>
+template <int D, int F>
 struct MState {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     f4_t acc[C::DPL];  // rows 4g..4g+3 of O x 2^6 (row h: hi part of head h, row h+8: lo part)
     float m;           // reference max of head n (log2 domain)
     float l;           // this lane's share of head n's softmax denominator
-    float vr;          // INT8: reference V scale of acc (uniform; 0 until a nonzero scale)
+    float vr;          // scaled formats: reference V scale of acc (uniform; 0 until a nonzero scale)
 };
 
 // The query operand of S^T = K . Q^T (B operand; lane (g, n) serves column n,
@@ -270,12 +324,12 @@ struct QOp<D, true> {
 
 // Scores of one tile, S^T = K . Q^T (K registers in operand order), times
 // `sl` (softmax scale x log2 e, x the tile's K scale for INT8).
-template <int D, bool I8>
-__device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, I8>::KLD], const QOp<D, I8>& qo,
-                                            float sl)
+template <int D, int F>
+__device__ __forceinline__ f4_t tile_scores(const u32x4 (&kop)[MCfg<D, F>::KLD],
+                                            const QOp<D, MCfg<D, F>::I8>& qo, float sl)
 {
-    using C = MCfg<D, I8>;
-    if constexpr (I8) {
+    using C = MCfg<D, F>;
+    if constexpr (C::I8) {
         i32x4 s1 = {0, 0, 0, 0}, s2 = {0, 0, 0, 0}, s3 = {0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < C::KLD; ++c) {
@@ -373,12 +427,14 @@ __device__ __forceinline__ void make_q(QOp<D, I8>& qo, const QRaw<D, I8>& qr)
 }
 
 // The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
-template <int D, bool I8>
-__device__ __forceinline__ uint32_t v_word(const MTile<D, I8>& t, int nb, int h)
+template <int D, int F>
+__device__ __forceinline__ uint32_t v_word(const MTile<D, F>& t, int nb, int h)
 {
-    if constexpr (I8) {
+    if constexpr (F == kKvI8) {
         return code_pair(word(t.v[2 * h], nb >> 2) ^ 0x80808080u,
                          word(t.v[2 * h + 1], nb >> 2) ^ 0x80808080u, nb & 3);
+    } else if constexpr (F == kKvF8) {
+        return e4m3_pair2(word(t.v[2 * h], nb >> 2), word(t.v[2 * h + 1], nb >> 2), nb & 3);
     } else {
         return half_pair(word(t.v[2 * h], nb >> 1), word(t.v[2 * h + 1], nb >> 1), nb & 1);
     }
@@ -386,23 +442,30 @@ __device__ __forceinline__ uint32_t v_word(const MTile<D, I8>& t, int nb, int h)
 
 // One slot: SLOT consecutive tiles of the partition. With TAIL, only the first
 // `valid0` token rows are live (none when valid0 <= 0); without, all are.
-template <int D, bool I8, int SLOT, bool TAIL>
-__device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (&t)[SLOT],
-                                         const QOp<D, I8>& qo, int valid0,
+template <int D, int F, int SLOT, bool TAIL>
+__device__ __forceinline__ void mprocess(MState<D, F>& st, const MTile<D, F> (&t)[SLOT],
+                                         const QOp<D, MCfg<D, F>::I8>& qo, int valid0,
                                          float scale_log2, const float (&ksc)[SLOT],
                                          const float (&vsc)[SLOT], int lane, float lo_sel,
                                          u32x4* kl)
 {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     const int g = lane >> 4;
     float sc[SLOT][4];
 #pragma unroll
     for (int u = 0; u < SLOT; ++u) {
         u32x4 kop[C::KLD];
 #pragma unroll
-        for (int c = 0; c < C::KLD; ++c) kop[c] = t[u].k[c];
-        k_to_operand<D, I8, C::KLD>(kop, kl + u * (C::TILE / 16), lane);
-        const f4_t s = tile_scores<D, I8>(kop, qo, I8 ? scale_log2 * ksc[u] : scale_log2);
+        for (int c = 0; c < C::KLD; ++c) {
+            if constexpr (F == kKvF8) {  // 8 codes -> 8 fp16 (x 2^-8)
+                const uint32_t w0 = t[u].k[c].x, w1 = t[u].k[c].y;
+                kop[c] = u32x4{e4m3_pair(w0, 0), e4m3_pair(w0, 2), e4m3_pair(w1, 0), e4m3_pair(w1, 2)};
+            } else {
+                kop[c] = t[u].k[c];
+            }
+        }
+        k_to_operand<D, F, C::KLD>(kop, kl + u * (C::TILE / 16), lane);
+        const f4_t s = tile_scores<D, F>(kop, qo, C::SCALED ? scale_log2 * ksc[u] : scale_log2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[u][i] = s[i];
     }
@@ -443,7 +506,7 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
         }
     }
 
-    // INT8: a lazy reference V scale, like the reference max. Each tile's
+    // Scaled formats: a lazy reference V scale, like the reference max. Each tile's
     // weights are multiplied by its V scale over the reference (<= 2, so P
     // keeps its fp16 range) and the products accumulate at the reference
     // scale; the reference only moves, rescaling the accumulators, when a
@@ -452,7 +515,7 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
     float vrel[SLOT];
 #pragma unroll
     for (int u = 0; u < SLOT; ++u) vrel[u] = 1.0f;
-    if constexpr (I8) {
+    if constexpr (C::SCALED) {
         float vmax = vsc[0];
 #pragma unroll
         for (int u = 1; u < SLOT; ++u) vmax = fmaxf(vmax, vsc[u]);
@@ -493,12 +556,12 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
             }
         }
         const h8_t pa = __builtin_bit_cast(h8_t, u32x4{pw[0], pw[1], pw[2], pw[3]});
-        const MTile<D, I8>& ta = t[2 * pr];
-        const MTile<D, I8>& tb = t[2 * pr + 1];
+        const MTile<D, F>& ta = t[2 * pr];
+        const MTile<D, F>& tb = t[2 * pr + 1];
 #pragma unroll
         for (int nb = 0; nb < C::DPL; ++nb) {
-            u32x4 vw = {v_word<D, I8>(ta, nb, 0), v_word<D, I8>(ta, nb, 1), v_word<D, I8>(tb, nb, 0),
-                        v_word<D, I8>(tb, nb, 1)};
+            u32x4 vw = {v_word<D, F>(ta, nb, 0), v_word<D, F>(ta, nb, 1), v_word<D, F>(tb, nb, 0),
+                        v_word<D, F>(tb, nb, 1)};
             if constexpr (TAIL)
                 vw &= u32x4{vmask[2 * pr][0], vmask[2 * pr][1], vmask[2 * pr + 1][0], vmask[2 * pr + 1][1]};
             st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(h8_t, vw), st.acc[nb],
@@ -508,27 +571,27 @@ __device__ __forceinline__ void mprocess(MState<D, I8>& st, const MTile<D, I8> (
 }
 
 // A slot, with the tail masking compiled in only where it can be needed.
-template <int D, bool I8, int SLOT>
-__device__ __forceinline__ void mslot(MState<D, I8>& st, const MTile<D, I8> (&t)[SLOT],
-                                      const QOp<D, I8>& qo, int valid0,
+template <int D, int F, int SLOT>
+__device__ __forceinline__ void mslot(MState<D, F>& st, const MTile<D, F> (&t)[SLOT],
+                                      const QOp<D, MCfg<D, F>::I8>& qo, int valid0,
                                       float scale_log2, const float (&ksc)[SLOT],
                                       const float (&vsc)[SLOT], int lane, float lo_sel, u32x4* kl)
 {
     if (valid0 >= 16 * SLOT)
-        mprocess<D, I8, SLOT, false>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
+        mprocess<D, F, SLOT, false>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
     else
-        mprocess<D, I8, SLOT, true>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
+        mprocess<D, F, SLOT, true>(st, t, qo, valid0, scale_log2, ksc, vsc, lane, lo_sel, kl);
 }
 
 // The end of one (sequence, KV head) segment of a share. If the segment is
 // the row's whole context its query heads' outputs are written; otherwise its
 // partial (acc, m, l) goes to slot `slot` of the share (0: the share's first
 // row, 1: its last) for the merge kernel.
-template <int D, bool I8>
-__device__ __forceinline__ void emit(MState<D, I8>& st, const DecodeArgs& a, int s, int kvh, int group,
+template <int D, int F>
+__device__ __forceinline__ void emit(MState<D, F>& st, const DecodeArgs& a, int s, int kvh, int group,
                                      int share, bool cut, int slot, int lane)
 {
-    using C = MCfg<D, I8>;
+    using C = MCfg<D, F>;
     const int g = lane >> 4, n = lane & 15;
     // fold the lo rows (8..15, lane groups 2 and 3) onto the hi rows (0..7,
     // lane groups 0 and 1); the denominator of head n, summed over the four
@@ -538,7 +601,7 @@ __device__ __forceinline__ void emit(MState<D, I8>& st, const DecodeArgs& a, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32, 64);
     const float lsum = sum_over_groups(st.l);
-    const float unscale = I8 ? kPUnscale * st.vr : kPUnscale;  // back to the data's scale
+    const float unscale = C::SCALED ? kPUnscale * st.vr : kPUnscale;  // back to the data's scale
     if (!cut) {
         const int64_t row0 = (int64_t)s * a.num_q_heads + (int64_t)kvh * group;
 #pragma unroll
@@ -574,10 +637,11 @@ __device__ __forceinline__ void emit(MState<D, I8>& st, const DecodeArgs& a, int
 // heads of one share, so the head tiles of each physical block (adjacent in
 // the pool) are read at about the same time, each head by the same compute
 // die throughout.
-template <int D, bool I8, int SLOT, int MINW>
+template <int D, int F, int SLOT, int MINW>
 __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int group)
 {
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
+    constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;
@@ -591,7 +655,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     // the current chunk's block ids (ids outside the pool as -1), staged in
     // LDS and read back as a broadcast per tile
     __shared__ int mbid[kMaxChunkBlocks];
-    __shared__ u32x4 kl[SLOT * MCfg<D, I8>::TILE / 16];  // K of one slot on its way to operand order
+    __shared__ u32x4 kl[SLOT * MCfg<D, F>::TILE / 16];  // K of one slot on its way to operand order
     // lane (g, n) serves head n mod 8 of the group; columns 8..15 repeat the
     // group so that rows 8..15 of P can carry the lo halves
     const int qh = n & 7;
@@ -658,11 +722,11 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     take_segment(cg);  // the share holds at least one tile
     int cc0 = 0;
     int tb[kIdRegs];
-    QRaw<D, I8> qraw;
+    QRaw<D, KI8> qraw;
     fetch_ids(cg, 0, tb);
-    fetch_q<D, I8>(qraw, q_row(cg.s), qh < group, g);
-    QOp<D, I8> qo;
-    MState<D, I8> st;
+    fetch_q<D, KI8>(qraw, q_row(cg.s), qh < group, g);
+    QOp<D, KI8> qo;
+    MState<D, F> st;
     while (true) {
         const int nloc = min(cg.nseg - cc0, kMaxChunkBlocks);
         const int jb = cg.j + cc0;  // first block of the chunk within the row
@@ -685,7 +749,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         // flight. Tiles past the chunk load nothing (zero-byte descriptors)
         // and all their rows are dead; the loop has no early exit, so the last
         // step may compute one empty slot.
-        MTile<D, I8> ring[2][SLOT];
+        MTile<D, F> ring[2][SLOT];
         float ks[2][SLOT], vs[2][SLOT];
         // a slot's ids are read from LDS one slot ahead of its loads
         auto read_ids = [&](int (&e)[SLOT], int j0_) {
@@ -695,7 +759,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         auto load_slot = [&](int r, const int (&e)[SLOT], int j0_) {
 #pragma unroll
             for (int u = 0; u < SLOT; ++u)
-                mload<D, I8>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u], vs[r][u]);
+                mload<D, F>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u], vs[r][u]);
         };
         int e0[SLOT], e1[SLOT];
         read_ids(e0, 0);
@@ -703,9 +767,9 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         load_slot(0, e0, 0);
 
         if (seg_first) {  // a new row: its query operand and a fresh state
-            make_q<D, I8>(qo, qraw);
+            make_q<D, KI8>(qo, qraw);
 #pragma unroll
-            for (int nb = 0; nb < MCfg<D, I8>::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int nb = 0; nb < MCfg<D, F>::DPL; ++nb) st.acc[nb] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
             st.m = -INFINITY;
             st.l = 0.0f;
             st.vr = 0.0f;
@@ -720,20 +784,20 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         }
         if (have_next) {
             fetch_ids(ng, nc0, tb);
-            if (nc0 == 0) fetch_q<D, I8>(qraw, q_row(ng.s), qh < group, g);
+            if (nc0 == 0) fetch_q<D, KI8>(qraw, q_row(ng.s), qh < group, g);
         }
 
         for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
             read_ids(e0, jj + 2 * SLOT);
             load_slot(1, e1, jj + SLOT);
             __builtin_amdgcn_sched_barrier(0);
-            mslot<D, I8, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0], lane,
+            mslot<D, F, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0], lane,
                                lo_sel, kl);
             __builtin_amdgcn_sched_barrier(0);
             read_ids(e1, jj + 3 * SLOT);
             load_slot(0, e0, jj + 2 * SLOT);
             __builtin_amdgcn_sched_barrier(0);
-            mslot<D, I8, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1], vs[1],
+            mslot<D, F, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1], vs[1],
                                lane, lo_sel, kl);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -741,7 +805,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         if (seg_last) {
             const int nblk = rows[cg.s + 1] - rows[cg.s];
             // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
-            emit<D, I8>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nblk,
+            emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nblk,
                         cg.s == s0 && cg.j == j0 ? 0 : 1, lane);
         }
         if (!have_next) break;
@@ -750,32 +814,36 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     }
 }
 
-template <int D, bool I8, int SLOT, int MINW>
+template <int D, int F, int SLOT, int MINW>
 hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
 {
     const int64_t waves = (int64_t)a.shares * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, I8, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, F, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a,
                        group);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_waves_per_cu(int, bool int8)
+int decode_waves_per_cu(int, int fmt)
 {
     // 4 SIMDs per compute unit x the waves per SIMD the register allocation
     // is bounded to; only a sizing hint for the number of shares
-    return 4 * (int8 ? PA_MINW_I8 : PA_MINW_F16);
+    return 4 * (fmt == kKvI8 ? PA_MINW_I8 : fmt == kKvF8 ? PA_MINW_F8 : PA_MINW_F16);
 }
 
-hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st)
+hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)
 {
-    if (head_dim == 128)
-        return int8 ? launch_waves<128, true, PA_SLOT_I8, PA_MINW_I8>(a, group, st)
-                    : launch_waves<128, false, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
-    if (head_dim == 64)
-        return int8 ? launch_waves<64, true, PA_SLOT_I8, PA_MINW_I8>(a, group, st)
-                    : launch_waves<64, false, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+    if (head_dim == 128) {
+        if (fmt == kKvI8) return launch_waves<128, kKvI8, PA_SLOT_I8, PA_MINW_I8>(a, group, st);
+        if (fmt == kKvF8) return launch_waves<128, kKvF8, PA_SLOT_F8, PA_MINW_F8>(a, group, st);
+        return launch_waves<128, kKvF16, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+    }
+    if (head_dim == 64) {
+        if (fmt == kKvI8) return launch_waves<64, kKvI8, PA_SLOT_I8, PA_MINW_I8>(a, group, st);
+        if (fmt == kKvF8) return launch_waves<64, kKvF8, PA_SLOT_F8, PA_MINW_F8>(a, group, st);
+        return launch_waves<64, kKvF16, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -8,6 +8,10 @@
 
 namespace pa {
 
+// KV cache formats of the decode: fp16, INT8 codes, FP8 (OCP E4M3) codes; the
+// code formats carry one fp32 scale per (block, KV head) for K and for V.
+enum KvFormat { kKvF16 = 0, kKvI8 = 1, kKvF8 = 2 };
+
 constexpr int kBlockTokens = 16;   // tokens per physical KV block
 constexpr int kMaxChunkBlocks = 256;  // block ids a decode wave stages in LDS at a time
 constexpr int kMaxGroup = 8;       // query heads per KV head
@@ -22,9 +26,9 @@ constexpr int kPrepThreads = 1024; // the prefix-sum kernel's one workgroup
 // second kernel.
 struct DecodeArgs {
     const void* q;          // fp16 [S][Hq][D]
-    const void* k;          // fp16 or int8 pool [NB][Hkv][16][D]
+    const void* k;          // fp16, int8 or E4M3 pool [NB][Hkv][16][D]
     const void* v;
-    const float* k_scale;   // INT8 only: [NB][Hkv]
+    const float* k_scale;   // INT8 and FP8: [NB][Hkv]
     const float* v_scale;
     const int32_t* tables;  // [S][max_blocks]
     const int32_t* ctx;     // [S]
@@ -60,15 +64,15 @@ __host__ __device__ inline int64_t ws_row_first_share(int S, int shares) { retur
 __host__ __device__ inline int64_t ws_row_last_share(int S, int shares) { return (int64_t)2 * S + 1 + shares; }
 
 // Work split (prefix sums) -> decode waves -> merge of cut rows, all on `st`.
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st);
-hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, bool int8, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);
+hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);
 // Decode waves each compute unit holds at once for this configuration.
-int decode_waves_per_cu(int head_dim, bool int8);
+int decode_waves_per_cu(int head_dim, int fmt);
 
 struct QuantArgs {
     const uint16_t* k;
     const uint16_t* v;
-    int8_t* kc;
+    int8_t* kc;             // INT8 codes, or FP8 (E4M3) codes as bytes
     int8_t* vc;
     float* ks;
     float* vs;
@@ -79,6 +83,7 @@ struct QuantArgs {
 };
 
 hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_quantize_fp8(const QuantArgs& a, int head_dim, hipStream_t st);
 
 // One new token per sequence into the paged cache (pa_append.hip).
 struct AppendArgs {

@@ -83,7 +83,29 @@ __device__ __forceinline__ uint32_t pack4(uint32_t w0, uint32_t w1, float scale,
     return __builtin_amdgcn_perm(t1, t0, 0x0C0C0400u) | __builtin_amdgcn_perm(t3, t2, 0x04000C0Cu);
 }
 
-template <int D>
+// FP8 (OCP E4M3) codes of the four fp16 values in words w0, w1, packed as
+// four bytes: the correctly rounded quotient x / scale (as for INT8, with
+// the sign of zero kept), then
+// the hardware's round-to-nearest-even conversion to E4M3 (|x / scale| <= 448,
+// so it never reaches the format's end).
+__device__ __forceinline__ uint32_t pack4_fp8(uint32_t w0, uint32_t w1, float scale, float r)
+{
+    const h2_t a = __builtin_bit_cast(h2_t, w0), b = __builtin_bit_cast(h2_t, w1);
+    float q[4] = {(float)a.x, (float)a.y, (float)b.x, (float)b.y};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float q0 = __fmul_rn(q[i], r);
+        const float e = __builtin_fmaf(-q0, scale, q[i]);
+        // the correction turns -0 into +0; the quotient keeps x's sign (E4M3
+        // has a negative zero)
+        q[i] = __builtin_copysignf(__builtin_fmaf(e, r, q0), q[i]);
+    }
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+    return (uint32_t)v;
+}
+
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
 {
     constexpr int kChunks = kBlockTokens * D * 2 / 16 / 64;  // 16-byte chunks per lane
@@ -116,7 +138,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
         for (int w = 0; w < 4; ++w)
             m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(h2_t, word(x[c], w) & 0x7FFF7FFFu));
     const float amax = wave_max(fmaxf((float)m2.x, (float)m2.y));
-    const float scale = amax / 127.0f;
+    const float scale = amax / (FP8 ? 448.0f : 127.0f);
     if (lane == 0) *sdst = scale;
     const float rcp = 1.0f / scale;  // correctly rounded; unused when scale is 0
 
@@ -124,8 +146,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
     for (int c = 0; c < kChunks; ++c) {
         u32x2 packed = {0u, 0u};
         if (scale != 0.0f) {
-            packed.x = pack4(word(x[c], 0), word(x[c], 1), scale, rcp);
-            packed.y = pack4(word(x[c], 2), word(x[c], 3), scale, rcp);
+            if (FP8) {
+                packed.x = pack4_fp8(word(x[c], 0), word(x[c], 1), scale, rcp);
+                packed.y = pack4_fp8(word(x[c], 2), word(x[c], 3), scale, rcp);
+            } else {
+                packed.x = pack4(word(x[c], 0), word(x[c], 1), scale, rcp);
+                packed.y = pack4(word(x[c], 2), word(x[c], 3), scale, rcp);
+            }
         }
         if (PA_Q_NT)
             __builtin_nontemporal_store(packed, dst + lane + 64 * c);
@@ -136,18 +163,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
 
 }  // namespace
 
-hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t st)
+template <bool FP8>
+hipError_t launch_quantize_fmt(const QuantArgs& a, int head_dim, hipStream_t st)
 {
     const int64_t tiles = 2 * a.num_ids * a.num_kv_heads;
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)((tiles + 3) / 4));
     if (head_dim == 64)
-        hipLaunchKernelGGL(quantize_kernel<64>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quantize_kernel<64, FP8>), grid, dim3(256), 0, st, a);
     else if (head_dim == 128)
-        hipLaunchKernelGGL(quantize_kernel<128>, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((quantize_kernel<128, FP8>), grid, dim3(256), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, int head_dim, hipStream_t st)
+{
+    return launch_quantize_fmt<false>(a, head_dim, st);
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, int head_dim, hipStream_t st)
+{
+    return launch_quantize_fmt<true>(a, head_dim, st);
 }
 
 }  // namespace pa

@@ -180,10 +180,11 @@ def test_workspace_and_share_sizing():
     # the mixed batch's shape: one share per resident wave (256 CUs x 4 SIMDs x
     # 1 fp16 / 2 INT8 waves per SIMD at head_dim 128) over 8 KV heads
     assert pa.pa_decode_shares(64, 8, 128, 1024) == 128
-    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_int8=True) == 256
+    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=pa.KV_INT8) == 256
+    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=pa.KV_FP8) == 256
     assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024)
             == ints(64, 128, 8) + 128 * 2 * 32 * 130 * 4)
-    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_int8=True)
+    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_format=pa.KV_INT8)
             == ints(64, 256, 8) + 256 * 2 * 32 * 130 * 4)
     # explicit share length: 1 x 1024 blocks x 16 tokens / 256 tokens
     assert pa.pa_decode_shares(1, 1, 64, 1024, 16, 256) == 64
