@@ -17,8 +17,8 @@
 // Three cache formats, one kernel template (F): fp16; INT8 codes with one
 // fp32 scale per (block, head) for K and for V; FP8 (OCP E4M3) codes with
 // the same scales (monograph section 5.1's FP8 variant). INT8 scores run on
-// the int8 matrix cores; FP8 tiles are widened to fp16 in registers and take
-// the fp16 path.
+// the int8 matrix cores; FP8 tiles are widened to fp16 in registers (the
+// hardware's E4M3 -> fp16 conversion) and take the fp16 path.
 //
 // Per 16-token tile, with the G <= 8 query heads of the KV head in the 16
 // columns of the MFMA tile:
@@ -147,28 +147,19 @@ __device__ __forceinline__ uint32_t half_pair(uint32_t w0, uint32_t w1, int h)
     return __builtin_amdgcn_perm(w1, w0, h ? 0x07060302u : 0x05040100u);
 }
 
-// E4M3 -> fp16 for two codes that sit in bits 8..15 and 24..31 of x: the
-// code's sign goes to the fp16 sign and its 7 exponent-and-mantissa bits to
-// fp16 bits 7..13, which makes the fp16 value exactly the code's value times
-// 2^-8 (E4M3 subnormals land on fp16 subnormals, the bias differs by 8). The
-// 2^8 is folded into the tile's scales.
-__device__ __forceinline__ uint32_t e4m3_hi_bytes_to_half2(uint32_t x)
+// E4M3 codes B, B+1 (B = 0 or 2) of word w as an fp16 pair: the hardware's
+// scaled conversion with scale 1, exact (every E4M3 value is an fp16 value).
+template <int B>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w)
 {
-    return (x & 0x80008000u) | ((x >> 1) & 0x3F803F80u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, B != 0));
 }
 
-// Codes b, b+1 of word w as an fp16 pair (x 2^-8).
-__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, int b)
-{
-    const uint32_t sel = 0x0Cu | ((uint32_t)b << 8) | (0x0Cu << 16) | ((uint32_t)(b + 1) << 24);
-    return e4m3_hi_bytes_to_half2(__builtin_amdgcn_perm(w, w, sel));
-}
-
-// Code b of words w0 and w1 as an fp16 pair (x 2^-8).
+// Code b of words w0 and w1 as an fp16 pair.
 __device__ __forceinline__ uint32_t e4m3_pair2(uint32_t w0, uint32_t w1, int b)
 {
-    const uint32_t sel = 0x0Cu | ((uint32_t)b << 8) | (0x0Cu << 16) | ((uint32_t)(4 + b) << 24);
-    return e4m3_hi_bytes_to_half2(__builtin_amdgcn_perm(w1, w0, sel));
+    const uint32_t sel = (uint32_t)b | ((uint32_t)(4 + b) << 8) | 0x0C0C0000u;
+    return e4m3_pair<0>(__builtin_amdgcn_perm(w1, w0, sel));
 }
 
 template <int D, int F>
@@ -185,8 +176,6 @@ struct MCfg {
     static constexpr int DPL = D / 16;         // V dims per lane
     static constexpr int VB = DPL * EB;        // V register bytes per lane per token
     static constexpr int SVB = DPL * SEB;      // V pool bytes per lane per token
-    // the E4M3 -> fp16 widening leaves values x 2^-8; the scales take the 2^8
-    static constexpr float SCALE_FIX = F == kKvF8 ? 256.0f : 1.0f;
 };
 
 template <int VB> struct VChunk;
@@ -224,8 +213,8 @@ __device__ __forceinline__ void mload(MTile<D, F>& t, const DecodeArgs& a, int b
     const int64_t b = in_pool ? bid : 0;
     if constexpr (C::SCALED) {  // uniform addresses: one scalar load each
         const int64_t si = b * a.num_kv_heads + kvh;
-        ksc = in_pool ? a.k_scale[si] * C::SCALE_FIX : 0.0f;
-        vsc = in_pool ? a.v_scale[si] * C::SCALE_FIX : 0.0f;
+        ksc = in_pool ? a.k_scale[si] : 0.0f;
+        vsc = in_pool ? a.v_scale[si] : 0.0f;
     }
     const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::STILE;
     const int bytes = in_pool ? C::STILE : 0;
@@ -457,9 +446,9 @@ __device__ __forceinline__ void mprocess(MState<D, F>& st, const MTile<D, F> (&t
         u32x4 kop[C::KLD];
 #pragma unroll
         for (int c = 0; c < C::KLD; ++c) {
-            if constexpr (F == kKvF8) {  // 8 codes -> 8 fp16 (x 2^-8)
+            if constexpr (F == kKvF8) {  // 8 codes -> 8 fp16
                 const uint32_t w0 = t[u].k[c].x, w1 = t[u].k[c].y;
-                kop[c] = u32x4{e4m3_pair(w0, 0), e4m3_pair(w0, 2), e4m3_pair(w1, 0), e4m3_pair(w1, 2)};
+                kop[c] = u32x4{e4m3_pair<0>(w0), e4m3_pair<2>(w0), e4m3_pair<0>(w1), e4m3_pair<2>(w1)};
             } else {
                 kop[c] = t[u].k[c];
             }
