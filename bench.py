@@ -14,7 +14,8 @@ context ~ U[512, 16384], 32 query heads / 8 KV heads, head_dim 128, groups of
 Prints one JSON line. `value` is context (KV) tokens attended per second over
 the step (both decodes: 2 x sum(ctx) per step); the per-call figures, the
 roofline of the dominant call and the oracle's CPU time on the same step are
-in the same line. After the timed steps the next token's append
+in the same line. After the timed steps the FP8 (OCP E4M3) cache's quantize
+and decode, the next token's append
 (pa_append_kv_f16 / pa_append_kv_int8) and the eviction choice
 (pa_evict_select, 15 % of the allocated blocks at 1,024, 16,384 and 65,536
 blocks) are timed on their own and reported under `paths`; neither is part
@@ -65,6 +66,8 @@ def main() -> int:
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (CPU timing and output check)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip timing the FP8 cache (quantize + decode) after the step")
     ap.add_argument("--no-evict", action="store_true",
                     help="skip timing the eviction choice after the step")
     ap.add_argument("--no-append", action="store_true",
@@ -233,6 +236,57 @@ def main() -> int:
             "fp16_max_abs": float(np.max(np.abs(out16_h - ref16))),
             "int8_max_abs": float(np.max(np.abs(out8_h - ref8))),
         }
+    # The FP8 (OCP E4M3) cache (timed on its own after the step, not part of
+    # it): quantize the live blocks, then decode over the FP8 codes.
+    if not args.no_fp8:
+        kf = torch.zeros(k16.shape, dtype=torch.uint8, device=dev)
+        vf = torch.zeros_like(kf)
+        kfs = torch.zeros_like(ks)
+        vfs = torch.zeros_like(ks)
+        outf = torch.empty_like(out16)
+        wsf = pa.workspace_for(q, kf, tables, args.partition_tokens)
+
+        def timed(fn, n=20):
+            for _ in range(3):
+                fn()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            torch.cuda.synchronize()
+            e[0].record()
+            for _ in range(n):
+                fn()
+            e[1].record()
+            torch.cuda.synchronize()
+            return e[0].elapsed_time(e[1]) / n
+
+        for name, fn, nbytes in (
+            ("quantize_fp8", lambda: pa.pa_quantize_kv_fp8(k16, v16, kf, vf, kfs, vfs, ids),
+             alg["quantize"]),
+            ("fp8", lambda: pa.pa_paged_decode_fp8(q, kf, vf, kfs, vfs, tables, ctx, outf,
+                                                   w.softmax_scale, args.partition_tokens, wsf),
+             alg["int8"]),
+        ):
+            t_ms = timed(fn)
+            gbs = nbytes / (t_ms * 1e-3) / 1e9
+            rec = {"ms": round(t_ms, 5), "alg_bytes": nbytes, "gbs": round(gbs, 1),
+                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            if name == "fp8":
+                rec["kv_tokens_per_s"] = round(sum_ctx / (t_ms * 1e-3), 1)
+            paths[name] = rec
+        if not args.no_cpu_baseline:
+            import oracle
+
+            okf, okfs = oracle.quantize_kv_fp8(w.k_pool, live)
+            ovf, ovfs = oracle.quantize_kv_fp8(w.v_pool, live)
+            reff = oracle.paged_decode_fp8(w.q, okf, ovf, okfs, ovfs, w.block_tables,
+                                           w.context_lens, w.softmax_scale)
+            gkf, gvf = kf.cpu().numpy(), vf.cpu().numpy()
+            gkfs, gvfs = kfs.cpu().numpy(), vfs.cpu().numpy()
+            result["parity"]["fp8_codes_scales_bit_exact"] = bool(
+                np.array_equal(gkf[live], okf[live]) and np.array_equal(gvf[live], ovf[live])
+                and np.array_equal(gkfs[live].view(np.uint32), okfs[live].view(np.uint32))
+                and np.array_equal(gvfs[live].view(np.uint32), ovfs[live].view(np.uint32)))
+            result["parity"]["fp8_max_abs"] = float(np.max(np.abs(outf.cpu().numpy() - reff)))
+
     # The append of the next token (timed on its own after the step, not part
     # of it): every sequence writes one K and one V row, fp16 and INT8.
     if not args.no_append:
