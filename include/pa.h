@@ -52,7 +52,9 @@ enum {
     PA_ERR_SHAPE = -2,       /* inconsistent or non-positive sizes */
     PA_ERR_UNSUPPORTED = -3, /* valid but not built: block_size, head_dim, group size, alignment */
     PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
-    PA_ERR_HIP = -5          /* a HIP call failed; see pa_error_string */
+    PA_ERR_HIP = -5,         /* a HIP call failed; see pa_error_string */
+    PA_ERR_FULL = -6,        /* block manager: no free block */
+    PA_ERR_STATE = -7        /* block manager: the block is not allocated */
 };
 
 /* Static description of a return code. For PA_ERR_HIP it names the last HIP
@@ -223,6 +225,61 @@ int pa_append_kv_int8(const void* k_new, const void* v_new, int8_t* k_cache, int
                       float* k_scale, float* v_scale, const int32_t* block_tables,
                       const int32_t* positions, int num_seqs, int num_kv_heads, int head_dim,
                       int block_size, int max_blocks_per_seq, int64_t num_blocks, void* stream);
+
+/* ---- Block manager (host) and block copy -------------------------------
+ * paged-attention-runtime summary, "CORE CAPABILITIES" 1 (fixed 16-token
+ * blocks, free-list allocator, reference counting, prefix sharing,
+ * copy-on-write, fragmentation metrics); PagedAttention & KV-Cache Memory
+ * Management glossary page (the prefix-sharing allocator). A manager owns
+ * the bookkeeping of one pool of num_blocks physical blocks: a reference
+ * count per block, an optional 64-bit prefix hash per block, a free list
+ * that hands out the lowest free id first, and a map from prefix hash to the
+ * live block holding it. It never touches device memory; every call is
+ * host-only, thread-safe (one call at a time per manager) and returns
+ * PA_OK, PA_ERR_NULL, PA_ERR_FULL or PA_ERR_STATE.
+ *
+ * pa_bm_create returns NULL for num_blocks <= 0 or > 2^31 - 1, block_size
+ * <= 0, or no host memory; pa_bm_destroy frees it (NULL is ignored).
+ * pa_bm_allocate: with prefix_hash non-NULL and cached, the cached block
+ *   gains a reference (*cache_hit = 1); otherwise the lowest free block gets
+ *   one reference (and the hash, if given): *cache_hit = 0; PA_ERR_FULL when
+ *   none is free. cache_hit may be NULL.
+ * pa_bm_share: one more reference to a live block (a fork).
+ * pa_bm_release: one reference fewer; at zero the block is free again and
+ *   its hash forgotten.
+ * pa_bm_copy_on_write: a block about to be written. Held once: *out_block =
+ *   block, *must_copy = 0. Shared: a fresh block (no hash) takes the
+ *   caller's reference, *out_block = it, *must_copy = 1 -- copy the block's
+ *   K/V (and scales) with pa_copy_blocks before writing; PA_ERR_FULL when
+ *   none is free.
+ * pa_bm_num_free: free blocks (or PA_ERR_NULL).
+ * pa_bm_refcounts: the n = num_blocks reference counts into host out[]
+ *   (PA_ERR_SHAPE for another n): the eviction choice's refcount input.
+ * pa_internal_fragmentation: for a batch's context lengths (host array), the
+ *   unused token slots of its blocks over all their slots,
+ *   1 - sum(ctx) / (block_size * sum(ceil(ctx / block_size))); 0 for none. */
+typedef struct pa_block_manager pa_block_manager;
+pa_block_manager* pa_bm_create(int64_t num_blocks, int block_size);
+void pa_bm_destroy(pa_block_manager* m);
+int pa_bm_allocate(pa_block_manager* m, const uint64_t* prefix_hash, int32_t* block, int* cache_hit);
+int pa_bm_share(pa_block_manager* m, int32_t block);
+int pa_bm_release(pa_block_manager* m, int32_t block);
+int pa_bm_copy_on_write(pa_block_manager* m, int32_t block, int32_t* out_block, int* must_copy);
+int64_t pa_bm_num_free(pa_block_manager* m);
+int pa_bm_refcounts(pa_block_manager* m, int32_t* out, int64_t n);
+double pa_internal_fragmentation(const int32_t* context_lens, int num_seqs, int block_size);
+
+/* Copy whole blocks on the device (the data half of copy-on-write): for each
+ * i, block dst_ids[i] of dst_pool receives the bytes_per_block bytes of
+ * block src_ids[i] of src_pool (pools laid out as [num_blocks][bytes_per_block];
+ * call once per K/V pool and once per scale array). Pairs naming a block
+ * outside [0, num_blocks) are skipped; destinations must be distinct and
+ * not sources of other pairs. Device pointers; one asynchronous kernel on
+ * `stream`. Returns PA_OK (num_pairs == 0 launches nothing), PA_ERR_NULL,
+ * PA_ERR_SHAPE, PA_ERR_UNSUPPORTED or PA_ERR_HIP. */
+int pa_copy_blocks(const void* src_pool, void* dst_pool, int64_t bytes_per_block,
+                   const int32_t* src_ids, const int32_t* dst_ids, int64_t num_pairs,
+                   int64_t num_blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,8 @@ PA_ERR_SHAPE = -2
 PA_ERR_UNSUPPORTED = -3
 PA_ERR_WORKSPACE = -4
 PA_ERR_HIP = -5
+PA_ERR_FULL = -6
+PA_ERR_STATE = -7
 
 EXPORTED = (
     "pa_error_string",
@@ -44,6 +46,16 @@ EXPORTED = (
     "pa_append_kv_f16",
     "pa_append_kv_int8",
     "pa_evict_select",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_allocate",
+    "pa_bm_share",
+    "pa_bm_release",
+    "pa_bm_copy_on_write",
+    "pa_bm_num_free",
+    "pa_bm_refcounts",
+    "pa_internal_fragmentation",
+    "pa_copy_blocks",
 )
 
 
@@ -89,6 +101,25 @@ def lib() -> C.CDLL:
         L.pa_append_kv_int8.restype = i32
         L.pa_evict_select.argtypes = [p, p, i64, i32, i64, p, p]
         L.pa_evict_select.restype = i32
+        L.pa_bm_create.argtypes = [i64, i32]
+        L.pa_bm_create.restype = p
+        L.pa_bm_destroy.argtypes = [p]
+        L.pa_bm_destroy.restype = None
+        L.pa_bm_allocate.argtypes = [p, p, p, p]
+        L.pa_bm_allocate.restype = i32
+        for n in ("pa_bm_share", "pa_bm_release"):
+            getattr(L, n).argtypes = [p, i32]
+            getattr(L, n).restype = i32
+        L.pa_bm_copy_on_write.argtypes = [p, i32, p, p]
+        L.pa_bm_copy_on_write.restype = i32
+        L.pa_bm_num_free.argtypes = [p]
+        L.pa_bm_num_free.restype = i64
+        L.pa_bm_refcounts.argtypes = [p, p, i64]
+        L.pa_bm_refcounts.restype = i32
+        L.pa_internal_fragmentation.argtypes = [p, i32, i32]
+        L.pa_internal_fragmentation.restype = C.c_double
+        L.pa_copy_blocks.argtypes = [p, p, i64, p, p, i64, i64, p]
+        L.pa_copy_blocks.restype = i32
         _lib = L
     return _lib
 
@@ -369,10 +400,91 @@ def pa_paged_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, con
         raise PagedAttentionError("pa_paged_decode_fp8", rc)
 
 
+class BlockManager:
+    """The library's host block manager for one pool (pa_bm_*): allocation
+    with optional prefix-hash sharing, references, copy-on-write."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self.num_blocks = int(num_blocks)
+        self._h = lib().pa_bm_create(self.num_blocks, int(block_size))
+        if not self._h:
+            raise ValueError("pa_bm_create failed (sizes or host memory)")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pa_bm_destroy(h)
+
+    def _check(self, fn, rc):
+        if rc:
+            raise PagedAttentionError(fn, rc)
+
+    def allocate(self, prefix_hash=None):
+        """(block id, cache hit)."""
+        b, hit = C.c_int32(), C.c_int()
+        hp = None if prefix_hash is None else C.byref(C.c_uint64(int(prefix_hash) & (2**64 - 1)))
+        self._check("pa_bm_allocate", lib().pa_bm_allocate(self._h, hp, C.byref(b), C.byref(hit)))
+        return int(b.value), bool(hit.value)
+
+    def share(self, block: int) -> None:
+        self._check("pa_bm_share", lib().pa_bm_share(self._h, int(block)))
+
+    def release(self, block: int) -> None:
+        self._check("pa_bm_release", lib().pa_bm_release(self._h, int(block)))
+
+    def copy_on_write(self, block: int):
+        """(block to write, whether its contents must first be copied)."""
+        b, copy = C.c_int32(), C.c_int()
+        self._check("pa_bm_copy_on_write",
+                    lib().pa_bm_copy_on_write(self._h, int(block), C.byref(b), C.byref(copy)))
+        return int(b.value), bool(copy.value)
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    def refcounts(self):
+        import numpy as np
+
+        out = np.zeros(self.num_blocks, np.int32)
+        self._check("pa_bm_refcounts",
+                    lib().pa_bm_refcounts(self._h, out.ctypes.data_as(C.c_void_p), out.size))
+        return out
+
+
+def pa_internal_fragmentation(context_lens, block_size: int = 16) -> float:
+    import numpy as np
+
+    c = np.ascontiguousarray(np.asarray(context_lens, np.int32))
+    return float(lib().pa_internal_fragmentation(c.ctypes.data_as(C.c_void_p), c.size,
+                                                 int(block_size)))
+
+
+def pa_copy_blocks(src_pool, dst_pool, src_ids, dst_ids, stream=None):
+    """Copy whole blocks (leading dimension) of src_pool into dst_pool on the GPU."""
+    import torch
+
+    _need(src_ids, "src_ids", torch.int32, 1)
+    _need(dst_ids, "dst_ids", torch.int32, 1)
+    if src_ids.numel() != dst_ids.numel():
+        raise ValueError("src_ids and dst_ids differ in length")
+    if tuple(src_pool.shape) != tuple(dst_pool.shape) or src_pool.dtype != dst_pool.dtype:
+        raise ValueError("pools must share shape and dtype")
+    if not (src_pool.is_contiguous() and dst_pool.is_contiguous()):
+        raise ValueError("pools must be contiguous")
+    nb = src_pool.shape[0]
+    bpb = src_pool.numel() // nb * src_pool.element_size()
+    rc = lib().pa_copy_blocks(_ptr(src_pool), _ptr(dst_pool), bpb, _ptr(src_ids), _ptr(dst_ids),
+                              src_ids.numel(), nb, _stream(src_pool, stream))
+    if rc:
+        raise PagedAttentionError("pa_copy_blocks", rc)
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
     "pa_append_kv_int8", "pa_evict_select", "pa_quantize_kv_fp8", "pa_paged_decode_fp8",
-    "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8",
+    "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8", "BlockManager", "pa_internal_fragmentation",
+    "pa_copy_blocks",
 ]

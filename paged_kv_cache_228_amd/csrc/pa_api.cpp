@@ -203,6 +203,8 @@ const char* pa_error_string(int code)
                    "1..8 query heads per KV head, 16-byte aligned buffers)";
         case PA_ERR_WORKSPACE: return "split-K workspace missing or too small";
         case PA_ERR_HIP: return g_hip_msg;
+        case PA_ERR_FULL: return "no free KV block (or a reference count at its limit)";
+        case PA_ERR_STATE: return "the block is not allocated";
         default: return "unknown error code";
     }
 }
@@ -291,6 +293,26 @@ int pa_paged_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_
                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens,
                          workspace, workspace_bytes, stream, pa::kKvF8);
+}
+
+int pa_copy_blocks(const void* src_pool, void* dst_pool, int64_t bytes_per_block,
+                   const int32_t* src_ids, const int32_t* dst_ids, int64_t num_pairs,
+                   int64_t num_blocks, void* stream)
+{
+    if (num_pairs < 0 || bytes_per_block <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!src_pool || !dst_pool || !src_ids || !dst_ids) return PA_ERR_NULL;
+    if (num_pairs > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    pa::CopyArgs a;
+    a.src = static_cast<const char*>(src_pool);
+    a.dst = static_cast<char*>(dst_pool);
+    a.src_ids = src_ids;
+    a.dst_ids = dst_ids;
+    a.bytes_per_block = bytes_per_block;
+    a.num_blocks = num_blocks;
+    a.num_pairs = num_pairs;
+    hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
 int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t num_blocks,

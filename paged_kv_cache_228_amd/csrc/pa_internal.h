@@ -115,4 +115,17 @@ struct EvictArgs {
 
 hipError_t launch_evict(const EvictArgs& a, hipStream_t st);
 
+// Block copy for copy-on-write (pa_copy.hip).
+struct CopyArgs {
+    const char* src;
+    char* dst;
+    const int32_t* src_ids;  // [num_pairs]
+    const int32_t* dst_ids;
+    int64_t bytes_per_block;
+    int64_t num_blocks;
+    int64_t num_pairs;
+};
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
+
 }  // namespace pa
