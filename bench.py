@@ -18,8 +18,9 @@ in the same line. After the timed steps the FP8 (OCP E4M3) cache's quantize
 and decode, the next token's append
 (pa_append_kv_f16 / pa_append_kv_int8) and the eviction choice
 (pa_evict_select, 15 % of the allocated blocks at 1,024, 16,384 and 65,536
-blocks) are timed on their own and reported under `paths`; neither is part
-of the step.
+blocks), the host block manager (this batch's tables built with prefix-hash
+sharing) and the copy-on-write block copy are timed on their own and
+reported under `paths`; none of them is part of the step.
 """
 
 import argparse
@@ -68,6 +69,8 @@ def main() -> int:
                     help="skip the oracle leg (CPU timing and output check)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip timing the FP8 cache (quantize + decode) after the step")
+    ap.add_argument("--no-blockmgr", action="store_true",
+                    help="skip timing the block manager and the block copy after the step")
     ap.add_argument("--no-evict", action="store_true",
                     help="skip timing the eviction choice after the step")
     ap.add_argument("--no-append", action="store_true",
@@ -336,6 +339,55 @@ def main() -> int:
                 and np.array_equal(gv.view(np.uint16), ov[touched].view(np.uint16))
                 and all(np.array_equal(g.view(np.uint8), r[touched].view(np.uint8))
                         for g, r in zip(g8, o8)))
+    # The block manager (host) and the block copy of copy-on-write (timed on
+    # their own): build this batch's block tables through the manager, the
+    # 64 prefix blocks of each group of 4 sequences shared by prefix hash,
+    # then release everything; copy 1,024 whole blocks (K and V) on the GPU.
+    if not args.no_blockmgr:
+        bm = pa.BlockManager(w.num_blocks)
+        nblk = [(int(n) + 15) // 16 for n in w.context_lens]
+        t0 = time.perf_counter()
+        held = []
+        for s_i, n in enumerate(nblk):
+            grp = s_i // 4
+            for j in range(n):
+                held.append(bm.allocate((grp << 20) | j if j < 64 else None)[0])
+        t1 = time.perf_counter()
+        for b in held:
+            bm.release(b)
+        t2 = time.perf_counter()
+        n_ops = 2 * len(held)
+        rec = {"ops": n_ops, "blocks_used": len(set(held)),
+               "blocks_match_batch": len(set(held)) == n_live,
+               "alloc_release_us_per_op": round((t2 - t0) * 1e6 / n_ops, 3),
+               "internal_fragmentation": round(pa.pa_internal_fragmentation(w.context_lens), 6),
+               "note": "host C++ behind a Python binding; the per-op time is mostly the binding"}
+        n_cp = 1024
+        rng_cp = np.random.default_rng(5)
+        src_cp = up(rng_cp.choice(w.num_blocks // 2, n_cp, replace=False).astype(np.int32))
+        dst_cp = up((w.num_blocks // 2 + rng_cp.choice(w.num_blocks // 2, n_cp, replace=False)).astype(np.int32))
+        k_cp, v_cp = torch.empty_like(k16), torch.empty_like(v16)
+
+        def cp():
+            pa.pa_copy_blocks(k16, k_cp, src_cp, dst_cp)
+            pa.pa_copy_blocks(v16, v_cp, src_cp, dst_cp)
+
+        for _ in range(3):
+            cp()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(20):
+            cp()
+        e[1].record()
+        torch.cuda.synchronize()
+        us = e[0].elapsed_time(e[1]) * 1e3 / 20
+        cp_bytes = 2 * n_cp * hkv * 16 * d * 2 * 2  # K and V blocks, read and written
+        rec["copy_blocks"] = {"blocks": n_cp, "us": round(us, 2), "bytes": cp_bytes,
+                              "gbs": round(cp_bytes / us / 1e3, 1)}
+        del k_cp, v_cp
+        paths["block_manager"] = rec
+
     # The eviction choice (timed on its own, not part of the step): 15 % of
     # the allocated blocks, at the README's pool sizes and on this batch's pool
     # with its reference counts; p50 of per-call event times like the README.
