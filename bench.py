@@ -20,7 +20,14 @@ and decode, the next token's append
 (pa_evict_select, 15 % of the allocated blocks at 1,024, 16,384 and 65,536
 blocks), the host block manager (this batch's tables built with prefix-hash
 sharing) and the copy-on-write block copy are timed on their own and
-reported under `paths`; none of them is part of the step.
+reported under `paths`; none of them is part of the step. So are the
+decode latencies of the four smaller configurations (tiny, the Qwen2-shaped
+layer at 1/4/8 sequences, the Gaussian and the heavy-tailed INT8 batches;
+fp16, INT8 and FP8 caches; median/p10/p90 of 200 replays of the call captured
+in a graph, each between its own event pair, and the median of eager calls;
+the last two also cold, their pools rotated over copies larger than 1 GiB),
+reported under `configs` with their quality against the fp32 computation on
+the fp16 cache, and the HBM rate torch's own copy and sum reach (`hbm_probe`).
 """
 
 import argparse
@@ -56,6 +63,150 @@ def measured_traffic(call: str, workload: str):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
+CONFIGS = (
+    ("tiny", lambda W: W.tiny()),
+    ("qwen2_s1", lambda W: W.qwen2_layer(1)),
+    ("qwen2_s4", lambda W: W.qwen2_layer(4)),
+    ("qwen2_s8", lambda W: W.qwen2_layer(8)),
+    ("int8_gaussian", lambda W: W.int8_gaussian()),
+    ("int8_heavy_tailed", lambda W: W.int8_heavy_tailed()),
+)
+# pools of these two fit, or nearly fit, the 256 MB last-level cache: they are
+# also timed cold, each launch on the next of several copies of the pools
+COLD = ("int8_gaussian", "int8_heavy_tailed")
+COLD_ROTATION_BYTES = 1 << 30
+
+
+def per_launch_us(torch, np, launch, n=200, warm=20):
+    """p10/p50/p90 of n launches, each between its own pair of events on the
+    current stream (the one the library launches on); launch(i) gets the
+    launch index."""
+    for i in range(warm):
+        launch(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return [round(float(x), 2) for x in np.percentile(t, [10, 50, 90])]
+
+
+def config_table(pa, W, torch, np, dev, with_oracle):
+    """Decode latency of every smaller configuration on the three caches, and
+    (with_oracle) each output's distance to the oracle's fp32 computation on
+    the fp16 cache (quality) and to the oracle's computation on the same codes
+    (parity), with the oracle's own time."""
+    if with_oracle:
+        import oracle
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    table = {}
+    for name, make in CONFIGS:
+        w = make(W)
+        q, tables, ctx = up(w.q), up(w.block_tables), up(w.context_lens)
+        k16, v16 = up(w.k_pool), up(w.v_pool)
+        ids = up(w.live_block_ids())
+        k8, kf = (torch.zeros(k16.shape, dtype=t, device=dev) for t in (torch.int8, torch.uint8))
+        v8, vf = torch.zeros_like(k8), torch.zeros_like(kf)
+        ks, vs, kfs, vfs = (torch.zeros(k16.shape[:2], dtype=torch.float32, device=dev)
+                            for _ in range(4))
+        pa.pa_quantize_kv_int8(k16, v16, k8, v8, ks, vs, ids)
+        pa.pa_quantize_kv_fp8(k16, v16, kf, vf, kfs, vfs, ids)
+        S, sum_ctx = w.num_seqs, int(w.context_lens.sum())
+        rec = {"num_seqs": S, "sum_ctx": sum_ctx, "q_heads": w.num_q_heads,
+               "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "pool_blocks": w.num_blocks}
+        outs = {}
+        for path, pools, fn, alg in (
+            ("fp16", (k16, v16), pa.pa_paged_decode_f16, W.algorithmic_bytes(w, 2, False)),
+            ("int8", (k8, v8, ks, vs), pa.pa_paged_decode_int8, W.algorithmic_bytes(w, 1, True)),
+            ("fp8", (kf, vf, kfs, vfs), pa.pa_paged_decode_fp8, W.algorithmic_bytes(w, 1, True)),
+        ):
+            out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            ws = pa.workspace_for(q, pools[0], tables, 0)
+            copies = [pools]
+            if name in COLD:
+                per_copy = sum(x.numel() * x.element_size() for x in pools)
+                copies += [tuple(x.clone() for x in pools)
+                           for _ in range(COLD_ROTATION_BYTES // per_copy)]
+
+            def launch(i, fn=fn, out=out, ws=ws, copies=copies, rotate=False):
+                c = copies[i % len(copies)] if rotate else copies[0]
+                fn(q, *c, tables, ctx, out, w.softmax_scale, 0, ws)
+
+            # eager: host work of the call (binding, checks, launches) included
+            # whenever the GPU waits for it
+            eager = per_launch_us(torch, np, launch)
+            # the call captured once per pool copy into a graph and replayed:
+            # the device time of its kernels and the gaps between them
+            graphs = []
+            for c in range(len(copies)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    launch(c, rotate=True)
+                graphs.append(g)
+            p10, p50, p90 = per_launch_us(torch, np, lambda i: graphs[0].replay())
+            r = {"p10_us": p10, "p50_us": p50, "p90_us": p90, "eager_p50_us": eager[1],
+                 "eager_p90_us": eager[2],
+                 "decode_tokens_per_s": round(S / (p50 * 1e-6), 1),
+                 "kv_tokens_per_s": round(sum_ctx / (p50 * 1e-6), 1), "alg_bytes": alg,
+                 "gbs": round(alg / p50 / 1e3, 1), "frac_of_peak": round(alg / p50 / 1e3 / HBM_PEAK_GBS, 4)}
+            launch(0)
+            outs[path] = out.cpu().numpy()
+            if len(copies) > 1:
+                c10, c50, c90 = per_launch_us(torch, np, lambda i: graphs[i % len(graphs)].replay())
+                r["cold"] = {"copies": len(copies), "p10_us": c10, "p50_us": c50, "p90_us": c90,
+                             "gbs": round(alg / c50 / 1e3, 1),
+                             "frac_of_peak": round(alg / c50 / 1e3 / HBM_PEAK_GBS, 4)}
+            del copies, graphs
+            rec[path] = r
+        if with_oracle:
+            live = w.live_block_ids()
+            t0 = time.perf_counter()
+            ref = oracle.decode_workload_f16(w)
+            rec["oracle_fp16_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+            rec["out_std"] = round(float(ref.std()), 6)
+            codes = {"int8": oracle.quantize_kv_int8, "fp8": oracle.quantize_kv_fp8}
+            same = {"fp16": ref}
+            for path, quant in codes.items():
+                kc, ksc = quant(w.k_pool, live)
+                vc, vsc = quant(w.v_pool, live)
+                dec = oracle.paged_decode_int8 if path == "int8" else oracle.paged_decode_fp8
+                same[path] = dec(w.q, kc, vc, ksc, vsc, w.block_tables, w.context_lens,
+                                 w.softmax_scale)
+            for path, o in outs.items():
+                err = o.astype(np.float64) - ref
+                rec[path]["vs_fp32"] = {"rmse": float(np.sqrt(np.mean(err * err))),
+                                        "max_abs": float(np.max(np.abs(err)))}
+                rec[path]["parity_max_abs"] = float(np.max(np.abs(o - same[path])))
+        table[name] = rec
+        del k16, v16, k8, v8, kf, vf
+        torch.cuda.empty_cache()
+    return table
+
+
+def hbm_probe(torch, np, dev):
+    """HBM rates of torch's own kernels, for context: the sum of a 4 GiB fp32
+    tensor (bytes read / time) and a 2 GiB device copy (bytes read + written /
+    time); medians of 10."""
+    res = {}
+    x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    src = torch.ones(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for key, fn, nbytes in (("sum_read_gbs", lambda: x.sum(), 1 << 32),
+                            ("copy_gbs", lambda: dst.copy_(src), 2 << 31)):
+        us = per_launch_us(torch, np, lambda i: fn(), n=10, warm=3)[1]
+        res[key] = round(nbytes / us / 1e3, 1)
+    del x, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,6 +226,9 @@ def main() -> int:
                     help="skip timing the eviction choice after the step")
     ap.add_argument("--no-append", action="store_true",
                     help="skip timing the next-token append calls after the step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration decode latencies, quality table and "
+                         "HBM probe after the step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes "
                          "(a known-size reference for HBM byte counters)")
@@ -224,12 +378,31 @@ def main() -> int:
         ref8 = oracle.decode_workload_int8(w, okc, ovc, oks, ovs)
         t3 = time.perf_counter()
         cpu_s = t3 - t0
+        # the same INT8 decode on one host thread, over the first two sequences
+        threads = oracle.max_threads()
+        one = np.arange(2, dtype=np.int32)
+        oracle.set_threads(1)
+        t4 = time.perf_counter()
+        oracle.paged_decode_int8(w.q, okc, ovc, oks, ovs, w.block_tables, w.context_lens,
+                                 w.softmax_scale, seq_ids=one)
+        t5 = time.perf_counter()
+        oracle.set_threads(threads)
+        cpu_model = ""
+        if os.path.exists("/proc/cpuinfo"):
+            with open("/proc/cpuinfo") as f:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                                  if ln.startswith("model name")), "")
         result["cpu_baseline"] = {
             "value": round(2 * sum_ctx / cpu_s, 1), "unit": "KV tokens/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": (f"one full step of the same batch: quantize of the {n_live} live blocks "
                        f"({t1 - t0:.2f}s), fp16 decode ({t2 - t1:.2f}s), INT8 decode "
                        f"({t3 - t2:.2f}s), all {S} sequences"),
+            "cpu_model": cpu_model,
+            "one_thread_int8_decode": {
+                "value": round(int(w.context_lens[:2].sum()) / (t5 - t4), 1), "unit": "KV tokens/s",
+                "sample": f"INT8 decode of the first 2 sequences ({int(w.context_lens[:2].sum())} "
+                          f"context tokens, {t5 - t4:.2f}s)"},
         }
         result["parity"] = {
             "codes_scales_bit_exact": bool(
@@ -418,6 +591,12 @@ def main() -> int:
                 rec["bit_exact"] = bool(np.array_equal(got, OE.evict_select(ref_h, last_h, 10_000, k_ev)))
             ev[str(nb_ev)] = rec
         paths["evict_select"] = ev
+
+    if not args.no_configs:
+        t_cfg = time.time()
+        result["configs"] = config_table(pa, W, torch, np, dev, not args.no_cpu_baseline)
+        result["hbm_probe"] = hbm_probe(torch, np, dev)
+        print(f"[bench] configs and probe in {time.time() - t_cfg:.1f}s", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
     return 0
 

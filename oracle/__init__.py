@@ -48,6 +48,8 @@ def lib() -> C.CDLL:
         L.pa_ref_half_to_float_array.restype = None
         L.pa_ref_max_threads.argtypes = []
         L.pa_ref_max_threads.restype = i32
+        L.pa_ref_set_threads.argtypes = [i32]
+        L.pa_ref_set_threads.restype = None
         L.pa_ref_quantize_kv_int8.argtypes = [p, p, p, p, i64, i64, i32, i32, i32]
         L.pa_ref_quantize_kv_int8.restype = i32
         common = [p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, p, i32, p, i32]
@@ -82,6 +84,11 @@ def _c(a, dtype):
 
 def max_threads() -> int:
     return int(lib().pa_ref_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Host threads the oracle's parallel loops use from now on."""
+    lib().pa_ref_set_threads(int(n))
 
 
 def half_to_float(bits: np.ndarray) -> np.ndarray:

@@ -74,6 +74,17 @@ void pa_ref_half_to_float_array(const uint16_t* h, float* out, int64_t n)
     for (int64_t i = 0; i < n; ++i) out[i] = pa_ref_half_to_float(h[i]);
 }
 
+/* Host threads the OpenMP loops use from now on (n <= 0 leaves it as it is);
+ * for timing the oracle on fewer cores. */
+void pa_ref_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int pa_ref_max_threads(void)
 {
 #ifdef _OPENMP
