@@ -8,34 +8,25 @@
 // q.k_t) v_t over the sequence's tokens, K/V reached through the block table
 // (glossary monograph, section 2.1).
 //
-// 1. prep, workgroup 0: the context lengths become tile prefix sums
-//    rows[s] = sum_{s' < s} ceil(ctx_s' / 16) (total T = rows[S]); for every
-//    share k of [0, T) the row holding its first tile k T / shares; for every
-//    sequence the first and last share holding its tiles. The other
-//    workgroups write the zero output rows of empty contexts.
+// 1. the work split: the context lengths become tile prefix sums
+//    rows[s] = sum_{s' < s} ceil(ctx_s' / 16) (total T = rows[S]). Up to
+//    kScanSeqs sequences every decode wave scans them itself; beyond that
+//    the prep kernel below does it once, before the waves, and also stores
+//    for every share k of [0, T) the row holding its first tile k T / shares.
 // 2. the decode waves (pa_decode_mfma.hip) stream their shares; rows inside
 //    one share are finished there, cut rows leave one partial per share.
 // 3. merge: one wave per (sequence, query head) of a cut row combines its
 //    partials (log-sum-exp: M = max m_k, out = sum 2^(m_k - M) acc_k /
-//    sum 2^(m_k - M) l_k).
+//    sum 2^(m_k - M) l_k); the rows of empty contexts are written as zeros.
 #include "pa_internal.h"
 #include "pa_split.h"
 
 namespace pa {
 namespace {
 
-__global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a, int head_dim)
+__global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a)
 {
     const int t = threadIdx.x;
-    if (blockIdx.x > 0) {  // zero rows of empty contexts, one sequence per step
-        const int64_t row_floats = (int64_t)a.num_q_heads * head_dim;
-        for (int s = blockIdx.x - 1; s < a.num_seqs; s += gridDim.x - 1) {
-            if (clamp_blocks(a.ctx[s], a.max_blocks) != 0) continue;
-            float* o = a.out + (int64_t)s * row_floats;
-            for (int64_t e = t; e < row_floats; e += kPrepThreads) o[e] = 0.0f;
-        }
-        return;
-    }
     __shared__ int wsum[kPrepThreads / 64];
     __shared__ int carry_s;
     const int lane = t & 63, w = t >> 6;
@@ -65,19 +56,11 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a,
 
     const int64_t T = carry, K = a.shares;
     int32_t* first_row = a.rows + ws_first_row(a.num_seqs);
-    int32_t* row_kf = a.rows + ws_row_first_share(a.num_seqs, a.shares);
-    int32_t* row_kl = a.rows + ws_row_last_share(a.num_seqs, a.shares);
     for (int s = t; s < a.num_seqs; s += kPrepThreads) {
         const int64_t r0 = a.rows[s], r1 = a.rows[s + 1];
-        if (r1 == r0) {  // empty: nothing to merge
-            row_kf[s] = row_kl[s] = 0;
-            continue;
-        }
         // shares whose first tile lies in [r0, r1)
         const int64_t k1 = min(first_share_at(r1, T, K), K);
         for (int64_t k = first_share_at(r0, T, K); k < k1; ++k) first_row[k] = s;
-        row_kf[s] = (int)share_of(r0, T, K);
-        row_kl[s] = (int)share_of(r1 - 1, T, K);
     }
 }
 
@@ -86,10 +69,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
 {
     const int hq = blockIdx.x, s = blockIdx.y;
     const int lane = threadIdx.x;
-    const int64_t kf = a.rows[ws_row_first_share(a.num_seqs, a.shares) + s];
-    const int64_t kl = a.rows[ws_row_last_share(a.num_seqs, a.shares) + s];
-    if (kf == kl) return;  // finished by its one share, or empty
-    const int64_t T = a.rows[a.num_seqs], K = a.shares, r0 = a.rows[s];
+    const int64_t r0 = a.rows[s], r1 = a.rows[s + 1], T = a.rows[a.num_seqs], K = a.shares;
+    float* o = a.out + ((int64_t)s * a.num_q_heads + hq) * D;
+    constexpr int NC = D / 64;
+    if (r1 == r0) {  // empty context: a zero row
+#pragma unroll
+        for (int c = 0; c < NC; ++c) o[lane + 64 * c] = 0.0f;
+        return;
+    }
+    // the first and the last share holding the row's tiles
+    const int64_t kf = share_of(r0, T, K), kl = share_of(r1 - 1, T, K);
+    if (kf == kl) return;  // finished by its one share
     const int kvh = hq / group, qi = hq - kvh * group;
     const int64_t nslot = K * a.num_kv_heads * 2 * group;
     // partial entry of share k (0 when it holds no tile of the row)
@@ -109,7 +99,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
     float mmax = mloc;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d, 64));
-    constexpr int NC = D / 64;
     float num[NC] = {};
     float den = 0.0f;
     for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
@@ -137,7 +126,6 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, 64);
-    float* o = a.out + ((int64_t)s * a.num_q_heads + hq) * D;
     const float inv = 1.0f / den;
 #pragma unroll
     for (int c = 0; c < NC; ++c) o[lane + 64 * c] = num[c] * inv;
@@ -147,10 +135,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)
 {
-    const int zero_groups = a.num_seqs < 256 ? a.num_seqs : 256;
-    hipLaunchKernelGGL(decode_prep_kernel, dim3(1 + zero_groups), dim3(kPrepThreads), 0, st, a, head_dim);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (a.num_seqs > kScanSeqs) {
+        hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(kPrepThreads), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     e = launch_decode_waves(a, head_dim, group, fmt, st);
     if (e != hipSuccess) return e;
     const dim3 grid(a.num_q_heads, a.num_seqs);

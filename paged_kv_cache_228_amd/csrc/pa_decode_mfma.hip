@@ -78,9 +78,11 @@ constexpr float kPUnscale = 1.0f / 64.0f;
 #define PA_KV_AUX 2
 #endif
 // Waves per SIMD the register allocation must leave room for. A ring of two
-// 4-tile fp16 slots needs more than half of the register file, so fp16 runs
-// one wave per SIMD with 32 KiB of loads in flight per wave; INT8 tiles are
-// half the size and run two.
+// 4-tile fp16 slots needs more than half of the register file, so fp16 is
+// bounded for one wave per SIMD with 32 KiB of loads in flight per wave;
+// INT8 and FP8 tiles are half the size and are bounded for two (256
+// registers), which compiled tighter code than the one-wave bound even
+// though the launch now places one wave per SIMD.
 #ifndef PA_MINW_F16
 #define PA_MINW_F16 1
 #endif
@@ -622,6 +624,73 @@ __device__ __forceinline__ void emit(MState<D, F>& st, const DecodeArgs& a, int 
     }
 }
 
+// This wave's place in the work split (pa_split.h): its share's tile range
+// [p0, p1) of the KV head's T tiles and the row s0 holding tile p0, whose
+// first tile is rs0. Up to kScanSeqs sequences the wave scans the context
+// lengths itself (four per lane) and the grid's first wave stores the prefix
+// sums rows[0..S] for the merge kernel; beyond that the prep kernel has stored
+// them, with the first row of every share.
+struct ShareLoc {
+    int64_t p0, p1;
+    int s0, rs0;
+};
+__device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share, int lane)
+{
+    static_assert(kScanSeqs == 4 * 64, "four sequences per lane");
+    const int S = a.num_seqs;
+    const int64_t K = a.shares;
+    ShareLoc r;
+    if (S > kScanSeqs) {
+        const int64_t T = a.rows[S];
+        r.p0 = share * T / K;
+        r.p1 = (share + 1) * T / K;
+        r.s0 = r.p0 < r.p1 ? a.rows[ws_first_row(S) + share] : 0;
+        r.rs0 = a.rows[r.s0];
+        return r;
+    }
+    int nb[4], ex[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int s = 64 * u + lane;
+        nb[u] = s < S ? clamp_blocks(a.ctx[s], a.max_blocks) : 0;
+    }
+    int carry = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // exclusive prefix sums, 64 rows at a time
+        int x = nb[u];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        ex[u] = carry + x - nb[u];
+        carry += __shfl(x, 63, 64);
+    }
+    if (blockIdx.x == 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (64 * u + lane < S) a.rows[64 * u + lane] = ex[u];
+        if (lane == 0) a.rows[S] = carry;
+    }
+    const int64_t T = uniform(carry);
+    r.p0 = share * T / K;
+    r.p1 = (share + 1) * T / K;
+    r.s0 = 0;
+    r.rs0 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // the one row with ex <= p0 < ex + nb, if p0 < T
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[u] > 0 && ex[u] <= r.p0 && r.p0 < ex[u] + nb[u]);
+        if (hit != 0) {
+            const int l = __builtin_ctzll(hit);
+            r.s0 = 64 * u + l;
+            r.rs0 = __shfl(ex[u], l, 64);
+        }
+    }
+    r.s0 = uniform(r.s0);
+    r.rs0 = uniform(r.rs0);
+    return r;
+}
+
 // One wave per (share, KV head): consecutive workgroups take consecutive KV
 // heads of one share, so the head tiles of each physical block (adjacent in
 // the pool) are read at about the same time, each head by the same compute
@@ -635,10 +704,8 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;
     const int g = lane >> 4, n = lane & 15;
-    const int32_t* rows = a.rows;  // tile prefix sums [S + 1], then first rows of shares
-    const int64_t total = rows[a.num_seqs];
-    const int64_t p0 = (int64_t)share * total / a.shares;
-    const int64_t p1 = (int64_t)(share + 1) * total / a.shares;
+    const ShareLoc loc = locate_share(a, share, lane);
+    const int64_t p0 = loc.p0, p1 = loc.p1;
     if (p0 >= p1) return;
 
     // the current chunk's block ids (ids outside the pool as -1), staged in
@@ -657,15 +724,16 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     // their first block at the start of the decode -- where sequences that
     // share a prefix keep their common blocks, now read by all of them at
     // about the same time, which the caches absorb.
+    auto nblk = [&](int r) { return clamp_blocks(a.ctx[r], a.max_blocks); };  // tiles of row r
     auto next_row = [&](int r) {  // the next row with tiles (exists while tiles remain)
         do {
             ++r;
-        } while (r < a.num_seqs - 1 && rows[r + 1] == rows[r]);
+        } while (r < a.num_seqs - 1 && nblk(r) == 0);
         return r;
     };
-    const int s0 = rows[a.num_seqs + 1 + share];  // the row holding tile p0
-    const int j0 = (int)(p0 - rows[s0]);
-    const int nseg0 = (int)min((int64_t)(rows[s0 + 1] - rows[s0] - j0), p1 - p0);
+    const int s0 = loc.s0;  // the row holding tile p0
+    const int j0 = (int)(p0 - loc.rs0);
+    const int nseg0 = (int)min((int64_t)(nblk(s0) - j0), p1 - p0);
     const bool deferred = j0 > 0 && p0 + nseg0 < p1;  // the first segment waits for the others
     int ws = deferred ? next_row(s0) : s0;  // the main walk's next segment
     int wj = deferred ? 0 : j0;
@@ -676,7 +744,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     };
     auto take_segment = [&](Seg& sg) {
         if (wpos < p1) {
-            sg = Seg{ws, wj, (int)min((int64_t)(rows[ws + 1] - rows[ws] - wj), p1 - wpos)};
+            sg = Seg{ws, wj, (int)min((int64_t)(nblk(ws) - wj), p1 - wpos)};
             wpos += sg.nseg;
             if (wpos < p1) {
                 ws = next_row(ws);
@@ -792,9 +860,9 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         }
 
         if (seg_last) {
-            const int nblk = rows[cg.s + 1] - rows[cg.s];
+            const int nb = nblk(cg.s);
             // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
-            emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nblk,
+            emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nb,
                         cg.s == s0 && cg.j == j0 ? 0 : 1, lane);
         }
         if (!have_next) break;
@@ -814,11 +882,13 @@ hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
 
 }  // namespace
 
-int decode_waves_per_cu(int, int fmt)
+int decode_waves_per_cu(int, int)
 {
-    // 4 SIMDs per compute unit x the waves per SIMD the register allocation
-    // is bounded to; only a sizing hint for the number of shares
-    return 4 * (fmt == kKvI8 ? PA_MINW_I8 : fmt == kKvF8 ? PA_MINW_F8 : PA_MINW_F16);
+    // One wave per SIMD (4 per compute unit), for every format: the INT8 and
+    // FP8 kernels are register-bounded for two waves per SIMD, but a second
+    // round of waves per SIMD ends measurably later than the first, and one
+    // wave per SIMD holding twice the tiles finished the mixed batch sooner.
+    return 4;
 }
 
 hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)

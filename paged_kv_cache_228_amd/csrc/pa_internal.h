@@ -23,7 +23,11 @@ constexpr int kPrepThreads = 1024; // the prefix-sum kernel's one workgroup
 // (share k: [k T / shares, (k + 1) T / shares)); one wave per (share, KV head).
 // A (sequence, KV head) row lying inside one share is finished by that wave;
 // a row cut by share boundaries leaves one partial per share, merged by a
-// second kernel.
+// second kernel. The tile prefix sums of the rows come from the context
+// lengths: up to kScanSeqs sequences, every decode wave scans them itself
+// (and the first wave stores them for the merge); beyond that, a one-workgroup
+// kernel runs first and stores them with the first row of every share.
+constexpr int kScanSeqs = 256;
 struct DecodeArgs {
     const void* q;          // fp16 [S][Hq][D]
     const void* k;          // fp16, int8 or E4M3 pool [NB][Hkv][16][D]
@@ -44,24 +48,21 @@ struct DecodeArgs {
     float scale_log2;       // softmax_scale * log2(e)
 };
 
-// Workspace, int32 part: tile prefix sums rows[S + 1]; the first row of
-// each share [shares]; per sequence the first and the last share holding its
-// tiles ([S] each; equal when one share holds them all or the context is
-// empty); padded to 256 bytes. Then fp32 partials: acc [shares][Hkv][2][G][D],
-// then m and l, each [shares][Hkv][2][G]; slot 0 of a share holds its first
-// row if that row is cut, slot 1 its last.
+// Workspace, int32 part: tile prefix sums rows[S + 1]; the first row of each
+// share [shares] (written only when S > kScanSeqs); padded to 256 bytes. Then
+// fp32 partials: acc [shares][Hkv][2][G][D], then m and l, each
+// [shares][Hkv][2][G]; slot 0 of a share holds its first row if that row is
+// cut, slot 1 its last.
 inline size_t workspace_int_bytes(int S, int shares)
 {
-    return ((size_t)(3 * (size_t)S + 1 + shares) * 4 + 255) & ~(size_t)255;
+    return ((size_t)((size_t)S + 1 + shares) * 4 + 255) & ~(size_t)255;
 }
 inline size_t workspace_bytes(int S, int Hq, int D, int shares)
 {
     return workspace_int_bytes(S, shares) + (size_t)shares * 2 * Hq * (size_t)(D + 2) * 4;
 }
-// Offsets (in int32) of the arrays after rows[S + 1].
+// Offset (in int32) of the share first rows after rows[S + 1].
 __host__ __device__ inline int64_t ws_first_row(int S) { return (int64_t)S + 1; }
-__host__ __device__ inline int64_t ws_row_first_share(int S, int shares) { return (int64_t)S + 1 + shares; }
-__host__ __device__ inline int64_t ws_row_last_share(int S, int shares) { return (int64_t)2 * S + 1 + shares; }
 
 // Work split (prefix sums) -> decode waves -> merge of cut rows, all on `st`.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);

@@ -170,22 +170,18 @@ def test_workspace_and_share_sizing():
     # Without a device to ask, the library sizes for 256 compute units.
     # A tiny batch: at most one share per 8 blocks of the 2 x 5-block bound.
     assert pa.pa_decode_shares(2, 2, 64, 5) == 2
-    # int32 prefix sums [S + 1], share first rows [K], first and last share
-    # of each sequence [S] x 2, padded to 256 B; then the partials:
-    # K x 2 slots x Hq x (D + 2) floats
+    # int32 prefix sums [S + 1], share first rows [K], padded to 256 B; then
+    # the partials: K x 2 slots x Hq x (D + 2) floats
     def ints(S, K, hkv):
-        return ((3 * S + 1 + K) * 4 + 255) // 256 * 256
+        return ((S + 1 + K) * 4 + 255) // 256 * 256
 
     assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5) == ints(2, 2, 2) + 2 * 2 * 4 * 66 * 4
-    # the mixed batch's shape: one share per resident wave (256 CUs x 4 SIMDs x
-    # 1 fp16 / 2 INT8 waves per SIMD at head_dim 128) over 8 KV heads
-    assert pa.pa_decode_shares(64, 8, 128, 1024) == 128
-    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=pa.KV_INT8) == 256
-    assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=pa.KV_FP8) == 256
-    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024)
-            == ints(64, 128, 8) + 128 * 2 * 32 * 130 * 4)
-    assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_format=pa.KV_INT8)
-            == ints(64, 256, 8) + 256 * 2 * 32 * 130 * 4)
+    # the mixed batch's shape: one share per wave, one wave per SIMD (256 CUs x
+    # 4 SIMDs) over 8 KV heads, whatever the cache format
+    for fmt in (pa.KV_F16, pa.KV_INT8, pa.KV_FP8):
+        assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=fmt) == 128
+        assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_format=fmt)
+                == ints(64, 128, 8) + 128 * 2 * 32 * 130 * 4)
     # explicit share length: 1 x 1024 blocks x 16 tokens / 256 tokens
     assert pa.pa_decode_shares(1, 1, 64, 1024, 16, 256) == 64
     # never more shares than blocks in the bound

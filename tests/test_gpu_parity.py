@@ -238,14 +238,17 @@ def test_int8_error_against_fp32_is_reported(name):
 
 
 @pytest.mark.parametrize("path", ["f16", "int8"])
-def test_many_short_sequences(path):
-    # more than 1024 sequences (the work split scans them in several passes),
-    # a tenth of them empty (zero rows written by the split's helper groups)
-    rng = np.random.default_rng(703)
-    ctx = rng.integers(1, 200, size=1500)
-    ctx[rng.random(1500) < 0.1] = 0
+@pytest.mark.parametrize("num_seqs", [256, 257, 1500])
+def test_many_short_sequences(path, num_seqs):
+    # up to 256 sequences every decode wave scans the context lengths itself;
+    # from 257 the prep kernel does it once (1500: in several passes of its
+    # 1024 threads); a tenth of the contexts empty (zero rows, written by the
+    # merge kernel)
+    rng = np.random.default_rng(703 + num_seqs)
+    ctx = rng.integers(1, 200, size=num_seqs)
+    ctx[rng.random(num_seqs) < 0.1] = 0
     w = W.build("many", 703, ctx, 4, 2, 64, num_blocks=int(((ctx + 15) // 16).sum()) + 8)
-    say(f"many short sequences {path}")
+    say(f"many short sequences {path} S={num_seqs}")
     if path == "f16":
         out = decode_f16(w)
         ref = oracle.decode_workload_f16(w)

@@ -3,13 +3,18 @@
 The decode cuts each KV head's tiles (all sequences in order, ceil(ctx / 16)
 per sequence) into K equal contiguous shares, share k = [k T / K, (k + 1) T / K)
 with integer division; pa_split.h and the prep, decode and merge kernels use
-the integer formulas restated below. These tests walk the shares the way the
-decode waves do and check that every tile is visited exactly once, that each
-cut (sequence, KV head) row leaves exactly one partial per share holding its
-tiles in a distinct (share, slot) place, and that the merge's share range and
-slot rule find exactly those partials -- including empty contexts and fewer
-tiles than shares. The GPU parity tests then compare the kernels' outputs with
-the oracle for many share counts.
+the integer formulas restated below. A wave finds the row holding its share's
+first tile either by its own scan of the context lengths (up to 256
+sequences: the row whose tile range contains the tile) or, for larger
+batches, from the prep kernel's table of share first rows; both are modelled
+and must agree. These tests walk the shares the way the decode waves do and
+check that every tile is visited exactly once, that each cut (sequence, KV
+head) row leaves exactly one partial per share holding its tiles in a
+distinct (share, slot) place, and that the merge's share range (first and
+last share from the row's prefix sums) and slot rule find exactly those
+partials -- including empty contexts and fewer tiles than shares. The GPU
+parity tests then compare the kernels' outputs with the oracle for many share
+counts.
 """
 
 import random
@@ -36,9 +41,8 @@ def walk(ctxs, K, max_blocks):
     for b in nblk:
         rows.append(rows[-1] + b)
     T = rows[S]
-    # prep: first row of every share; first / last share of every row
+    # prep (large batches): first row of every share
     first_row = [None] * K
-    kf_kl = {}
     for s in range(S):
         r0, r1 = rows[s], rows[s + 1]
         if r0 == r1:
@@ -46,9 +50,22 @@ def walk(ctxs, K, max_blocks):
         for k in range(first_share_at(r0, T, K), min(first_share_at(r1, T, K), K)):
             assert first_row[k] is None
             first_row[k] = s
-        kf_kl[s] = (share_of(r0, T, K), share_of(r1 - 1, T, K))
     if T:
         assert None not in first_row
+
+    # a wave's own scan (small batches): the one row with rows[s] <= p0 < rows[s + 1]
+    def scan_first_row(p0):
+        hits = [s for s in range(S) if nblk[s] > 0 and rows[s] <= p0 < rows[s] + nblk[s]]
+        assert len(hits) == (1 if p0 < T else 0)
+        return hits[0] if hits else 0
+
+    for k in range(K):
+        p0 = k * T // K
+        if p0 < (k + 1) * T // K:
+            assert scan_first_row(p0) == first_row[k]
+    # merge: first / last share of every row, from its prefix sums
+    kf_kl = {s: (share_of(rows[s], T, K), share_of(rows[s + 1] - 1, T, K))
+             for s in range(S) if rows[s + 1] > rows[s]}
     # decode waves: a share's later segments (each from a row's first block)
     # first, its first segment (which may start mid-row) last
     def next_row(r):
