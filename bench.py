@@ -23,9 +23,11 @@ sharing) and the copy-on-write block copy are timed on their own and
 reported under `paths`; none of them is part of the step. So are the
 decode latencies of the four smaller configurations (tiny, the Qwen2-shaped
 layer at 1/4/8 sequences, the Gaussian and the heavy-tailed INT8 batches;
-fp16, INT8 and FP8 caches; median/p10/p90 of 200 replays of the call captured
-in a graph, each between its own event pair, and the median of eager calls;
-the last two also cold, their pools rotated over copies larger than 1 GiB),
+fp16, INT8 and FP8 caches; per call, median/p10/p90 over 50 replays of a
+graph of 20 back-to-back calls, each replay between its own event pair, and
+the median of 200 eager calls, each between its own event pair; the last two
+configurations also cold, each call of the graph on the next of several pool
+copies that together exceed 1 GiB),
 reported under `configs` with their quality against the fp32 computation on
 the fp16 cache, and the HBM rate torch's own copy and sum reach (`hbm_probe`).
 """
@@ -75,6 +77,7 @@ CONFIGS = (
 # also timed cold, each launch on the next of several copies of the pools
 COLD = ("int8_gaussian", "int8_heavy_tailed")
 COLD_ROTATION_BYTES = 1 << 30
+GRAPH_CALLS = 20  # decode calls per captured graph in the per-configuration latencies
 
 
 def per_launch_us(torch, np, launch, n=200, warm=20):
@@ -142,15 +145,24 @@ def config_table(pa, W, torch, np, dev, with_oracle):
             # eager: host work of the call (binding, checks, launches) included
             # whenever the GPU waits for it
             eager = per_launch_us(torch, np, launch)
-            # the call captured once per pool copy into a graph and replayed:
-            # the device time of its kernels and the gaps between them
-            graphs = []
-            for c in range(len(copies)):
+            # GRAPH_CALLS back-to-back calls captured into one graph and
+            # replayed: per call, the device time of its kernels and the gaps
+            # between them, without the host's launch cost. The warm graph
+            # reuses the first pool copy; the cold one moves to the next copy
+            # at every call.
+            def graph_of(rotate):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g):
-                    launch(c, rotate=True)
-                graphs.append(g)
-            p10, p50, p90 = per_launch_us(torch, np, lambda i: graphs[0].replay())
+                    for c in range(GRAPH_CALLS):
+                        launch(c, rotate=rotate)
+                return g
+
+            def per_call(g):
+                return [round(x / GRAPH_CALLS, 2)
+                        for x in per_launch_us(torch, np, lambda i: g.replay(), n=50, warm=5)]
+
+            warm_graph = graph_of(False)
+            p10, p50, p90 = per_call(warm_graph)
             r = {"p10_us": p10, "p50_us": p50, "p90_us": p90, "eager_p50_us": eager[1],
                  "eager_p90_us": eager[2],
                  "decode_tokens_per_s": round(S / (p50 * 1e-6), 1),
@@ -159,11 +171,11 @@ def config_table(pa, W, torch, np, dev, with_oracle):
             launch(0)
             outs[path] = out.cpu().numpy()
             if len(copies) > 1:
-                c10, c50, c90 = per_launch_us(torch, np, lambda i: graphs[i % len(graphs)].replay())
+                c10, c50, c90 = per_call(graph_of(True))
                 r["cold"] = {"copies": len(copies), "p10_us": c10, "p50_us": c50, "p90_us": c90,
                              "gbs": round(alg / c50 / 1e3, 1),
                              "frac_of_peak": round(alg / c50 / 1e3 / HBM_PEAK_GBS, 4)}
-            del copies, graphs
+            del copies, warm_graph
             rec[path] = r
         if with_oracle:
             live = w.live_block_ids()
