@@ -20,7 +20,8 @@ and decode, the next token's append
 (pa_evict_select, 15 % of the allocated blocks at 1,024, 16,384 and 65,536
 blocks), the host block manager (this batch's tables built with prefix-hash
 sharing) and the copy-on-write block copy are timed on their own and
-reported under `paths`; none of them is part of the step. So are the
+reported under `paths`; none of them is part of the step, and neither are
+the two decodes timed again as back-to-back calls (`paths.*.back_to_back`). So are the
 decode latencies of the four smaller configurations (tiny, the Qwen2-shaped
 layer at 1/4/8 sequences, the Gaussian and the heavy-tailed INT8 batches;
 fp16, INT8 and FP8 caches; per call, median/p10/p90 over 50 replays of a
@@ -320,6 +321,29 @@ def main() -> int:
 
     ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
           for i, name in enumerate(["quantize", "fp16", "int8"])}
+
+    # Each decode also timed on its own after the steps (not part of them):
+    # the mean of 20 back-to-back calls between one event pair. Inside the
+    # step the INT8 decode reads codes that its quantize has just written,
+    # which the memory system makes a few microseconds slower to read.
+    def back_to_back(fn, n=20):
+        for _ in range(3):
+            fn()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(n):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / n
+
+    b2b = {
+        "fp16": back_to_back(lambda: pa.pa_paged_decode_f16(
+            q, k16, v16, tables, ctx, out16, w.softmax_scale, args.partition_tokens, ws16)),
+        "int8": back_to_back(lambda: pa.pa_paged_decode_int8(
+            q, k8, v8, ks, vs, tables, ctx, out8, w.softmax_scale, args.partition_tokens, ws8)),
+    }
     ms_step = wall * 1e3 / args.steps
     sum_ctx = int(w.context_lens.sum())
     S, d, hkv = w.num_seqs, w.head_dim, w.num_kv_heads
@@ -339,6 +363,9 @@ def main() -> int:
         if name != "quantize":
             rec["decode_tokens_per_s"] = round(S / t, 1)
             rec["kv_tokens_per_s"] = round(sum_ctx / t, 1)
+            g = alg[name] / (b2b[name] * 1e-3) / 1e9
+            rec["back_to_back"] = {"ms": round(b2b[name], 5), "gbs": round(g, 1),
+                                   "frac_of_peak": round(g / HBM_PEAK_GBS, 4)}
         paths[name] = rec
     dom = max(paths, key=lambda n: paths[n]["ms"])
     call = {"quantize": "pa_quantize_kv_int8", "fp16": "pa_paged_decode_f16",

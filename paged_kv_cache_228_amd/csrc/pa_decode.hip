@@ -64,6 +64,8 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a)
     }
 }
 
+constexpr int kMergeShares = 8;
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int group)
 {
@@ -89,43 +91,39 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
         const int slot = (k == kf && k * T / K < r0) ? 1 : 0;
         return ((k * a.num_kv_heads + kvh) * 2 + slot) * group + qi;
     };
-    // max of the partials' reference maxima: one share per lane
-    float mloc = -INFINITY;
-    for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
-        bool live;
-        const int64_t e = entry(k0 + lane, live);
-        if (live) mloc = fmaxf(mloc, a.part[nslot * D + e]);
-    }
-    float mmax = mloc;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, d, 64));
+    // kMergeShares shares per round, their m, l and acc loads all in flight
+    // together (rows rarely span more); across rounds a running maximum M
+    // rescales what has been summed (the log-sum-exp combine, one round at a
+    // time)
     float num[NC] = {};
-    float den = 0.0f;
-    for (int64_t k0 = kf; k0 <= kl; k0 += 64) {
-        bool live;
-        const int64_t e = entry(k0 + lane, live);
-        const float wk = live ? __builtin_amdgcn_exp2f(a.part[nslot * D + e] - mmax) : 0.0f;
-        den += live ? wk * a.part[nslot * (D + 1) + e] : 0.0f;
-        const int nk = (int)min((int64_t)64, kl - k0 + 1);
-        for (int i0 = 0; i0 < nk; i0 += 4) {  // four shares at a time, dims across lanes
-            float x[4][NC];
+    float den = 0.0f, M = -INFINITY;
+    for (int64_t k0 = kf; k0 <= kl; k0 += kMergeShares) {
+        float m[kMergeShares], l[kMergeShares], x[kMergeShares][NC];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                bool li;
-                const int64_t ek = entry(k0 + i0 + u, li);
+        for (int u = 0; u < kMergeShares; ++u) {
+            bool live;
+            const int64_t e = entry(k0 + u, live);
+            m[u] = live ? a.part[nslot * D + e] : -INFINITY;
+            l[u] = live ? a.part[nslot * (D + 1) + e] : 0.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) x[u][c] = (i0 + u < nk && li) ? a.part[ek * D + lane + 64 * c] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float w = __shfl(wk, (i0 + u) & 63, 64);  // 0 for shares past the row
-#pragma unroll
-                for (int c = 0; c < NC; ++c) num[c] += w * x[u][c];
-            }
+            for (int c = 0; c < NC; ++c) x[u][c] = live ? a.part[e * D + lane + 64 * c] : 0.0f;
         }
-    }
+        float mn = M;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, 64);
+        for (int u = 0; u < kMergeShares; ++u) mn = fmaxf(mn, m[u]);
+        const float al = mn == M ? 1.0f : __builtin_amdgcn_exp2f(M - mn);  // 0 on the first round
+        den *= al;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) num[c] *= al;
+#pragma unroll
+        for (int u = 0; u < kMergeShares; ++u) {
+            const float w = m[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[u] - mn);
+            den += w * l[u];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) num[c] += w * x[u][c];
+        }
+        M = mn;
+    }
     const float inv = 1.0f / den;
 #pragma unroll
     for (int c = 0; c < NC; ++c) o[lane + 64 * c] = num[c] * inv;
