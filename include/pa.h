@@ -97,7 +97,8 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
 
 /* Work split of the decode calls. For every KV head the tiles of all
  * sequences, in sequence order, are cut into equal contiguous shares, one
- * 64-lane wave each; a (sequence, KV head) whose tiles fall in one share is
+ * 64-lane wave each (one wave per SIMD of the device when partition_tokens is
+ * 0); a (sequence, KV head) whose tiles fall in one share is
  * finished by that wave, one cut by share boundaries is completed by a merge
  * kernel from the shares' partial results (log-sum-exp combine).
  * partition_tokens: the wanted tokens per share for the longest possible
@@ -124,9 +125,9 @@ size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads
  *     out[s][h] = sum_t softmax_t(softmax_scale * q[s][h] . k_t) * v_t
  * computed with a single-pass online softmax in fp32 (paged-attention-runtime
  * summary, "CORE CAPABILITIES" 2; glossary monograph section 5.2,
- * softmax(Q K^T / sqrt(d))). Three stream-ordered kernels: the work split
- * (prefix sums of the context lengths), the decode waves and the merge (see
- * pa_decode_shares). workspace: at least pa_decode_workspace_bytes(...) bytes
+ * softmax(Q K^T / sqrt(d))). Two stream-ordered kernels, the decode waves
+ * and the merge (see pa_decode_shares); above 256 sequences a third, the
+ * work split (prefix sums of the context lengths), runs first. workspace: at least pa_decode_workspace_bytes(...) bytes
  * of device memory owned by the caller, overwritten by every call; calls that
  * share a workspace must not overlap. num_seqs may be 0 (nothing is
  * launched, workspace may be NULL). */
