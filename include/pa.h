@@ -97,14 +97,14 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
 
 /* Work split of the decode calls. For every KV head the tiles of all
  * sequences, in sequence order, are cut into equal contiguous shares, one
- * 64-lane wave each (one wave per SIMD of the device when partition_tokens is
- * 0); a (sequence, KV head) whose tiles fall in one share is
+ * 64-lane wave each; a (sequence, KV head) whose tiles fall in one share is
  * finished by that wave, one cut by share boundaries is completed by a merge
  * kernel from the shares' partial results (log-sum-exp combine).
  * partition_tokens: the wanted tokens per share for the longest possible
  * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
- * to let the library size one share per wave the current device holds at
- * once. kv_format: 0 for pa_paged_decode_f16, 1 for pa_paged_decode_int8, 2
+ * to let the library size one wave per SIMD of the current device over the
+ * KV heads (fewer for small batches: at least 8 blocks of that longest batch
+ * per share). kv_format: 0 for pa_paged_decode_f16, 1 for pa_paged_decode_int8, 2
  * for pa_paged_decode_fp8 (other values are rejected).
  *
  * pa_decode_shares returns the number of shares per KV head, or a negative
