@@ -282,6 +282,19 @@ int pa_copy_blocks(const void* src_pool, void* dst_pool, int64_t bytes_per_block
                    const int32_t* src_ids, const int32_t* dst_ids, int64_t num_pairs,
                    int64_t num_blocks, void* stream);
 
+/* Measurement utility: the HBM read bandwidth a plain streaming read reaches
+ * on this device, the practical ceiling next to which the decode's achieved
+ * GB/s is read (the decode's bytes are HBM reads; nothing on the pages fixes
+ * the ceiling). Reads the `bytes` bytes at device pointer `src` once, with
+ * 16-byte non-temporal loads spread over `workgroups` workgroups of 256 lanes
+ * (grid-stride over 32 KiB chunks), and writes the XOR of the 32-bit words
+ * each workgroup read to sink[workgroup] (device memory, `workgroups`
+ * entries), so the result depends on every byte. One asynchronous kernel on
+ * `stream`. Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (bytes or workgroups
+ * <= 0), PA_ERR_UNSUPPORTED (bytes not a multiple of 16, or src not 16-byte
+ * aligned) or PA_ERR_HIP. */
+int pa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

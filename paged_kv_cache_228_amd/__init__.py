@@ -56,6 +56,7 @@ EXPORTED = (
     "pa_bm_refcounts",
     "pa_internal_fragmentation",
     "pa_copy_blocks",
+    "pa_hbm_read_probe",
 )
 
 
@@ -120,6 +121,8 @@ def lib() -> C.CDLL:
         L.pa_internal_fragmentation.restype = C.c_double
         L.pa_copy_blocks.argtypes = [p, p, i64, p, p, i64, i64, p]
         L.pa_copy_blocks.restype = i32
+        L.pa_hbm_read_probe.argtypes = [p, i64, p, i32, p]
+        L.pa_hbm_read_probe.restype = i32
         _lib = L
     return _lib
 
@@ -480,11 +483,26 @@ def pa_copy_blocks(src_pool, dst_pool, src_ids, dst_ids, stream=None):
         raise PagedAttentionError("pa_copy_blocks", rc)
 
 
+def pa_hbm_read_probe(src, sink, stream=None):
+    """Read every byte of the device tensor `src` once (16-byte non-temporal
+    loads, one workgroup per element of the int32 device tensor `sink`), the
+    XOR of each workgroup's 32-bit words written to its sink element."""
+    import torch
+
+    _need(sink, "sink", torch.int32, 1)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    rc = lib().pa_hbm_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 sink.numel(), _stream(src, stream))
+    if rc:
+        raise PagedAttentionError("pa_hbm_read_probe", rc)
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
     "pa_append_kv_int8", "pa_evict_select", "pa_quantize_kv_fp8", "pa_paged_decode_fp8",
     "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8", "BlockManager", "pa_internal_fragmentation",
-    "pa_copy_blocks",
+    "pa_copy_blocks", "pa_hbm_read_probe",
 ]

@@ -25,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "pa_decode.hip", "pa_decode_mfma.hip", "pa_quantize.hip", "pa_append.hip",
-           "pa_evict.hip", "pa_copy.hip", "pa_blockmgr.cpp"]
+           "pa_evict.hip", "pa_copy.hip", "pa_probe.hip", "pa_blockmgr.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -315,6 +315,19 @@ int pa_copy_blocks(const void* src_pool, void* dst_pool, int64_t bytes_per_block
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }
 
+int pa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int workgroups, void* stream)
+{
+    if (!src || !sink) return PA_ERR_NULL;
+    if (bytes <= 0 || workgroups <= 0) return PA_ERR_SHAPE;
+    if (bytes % 16 || !aligned16(src)) return PA_ERR_UNSUPPORTED;
+    pa::ProbeArgs a;
+    a.src = src;
+    a.words = bytes / 16;
+    a.sink = sink;
+    hipError_t e = pa::launch_read_probe(a, workgroups, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
 int pa_evict_select(const int32_t* refcount, const int32_t* last_used, int64_t num_blocks,
                     int32_t current_tick, int64_t k, int32_t* out_ids, void* stream)
 {

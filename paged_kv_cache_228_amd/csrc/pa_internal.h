@@ -129,4 +129,13 @@ struct CopyArgs {
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 
+// HBM read-bandwidth probe (pa_probe.hip).
+struct ProbeArgs {
+    const void* src;  // 16-byte aligned
+    int64_t words;    // 16-byte words to read
+    uint32_t* sink;   // [workgroups]
+};
+
+hipError_t launch_read_probe(const ProbeArgs& a, int workgroups, hipStream_t st);
+
 }  // namespace pa

@@ -213,3 +213,18 @@ def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypa
     assert bench.measured_traffic("pa_paged_decode_f16", "other") is None
     src.write_text("kernel v2\n")
     assert bench.measured_traffic("pa_paged_decode_f16", "wl") is None
+
+
+@pytest.mark.parametrize(
+    "args, code",
+    [
+        ((None, 1024, FAKE, 4), pa.PA_ERR_NULL),
+        ((FAKE, 1024, None, 4), pa.PA_ERR_NULL),
+        ((FAKE, 0, FAKE, 4), pa.PA_ERR_SHAPE),
+        ((FAKE, 1024, FAKE, 0), pa.PA_ERR_SHAPE),
+        ((FAKE, 1000, FAKE, 4), pa.PA_ERR_UNSUPPORTED),  # not a multiple of 16 bytes
+        ((FAKE + 8, 1024, FAKE, 4), pa.PA_ERR_UNSUPPORTED),  # not 16-byte aligned
+    ],
+)
+def test_read_probe_rejects_bad_arguments_on_host(args, code):
+    assert pa.lib().pa_hbm_read_probe(*args, None) == code
