@@ -290,6 +290,7 @@ struct MState {
     float m;           // reference max of head n (log2 domain)
     float l;           // this lane's share of head n's softmax denominator
     float vr;          // scaled formats: reference V scale of acc (uniform; 0 until a nonzero scale)
+    float vinv;        // 1 / vr (0 while vr is 0), recomputed only when vr moves
 };
 
 // The query operand of S^T = K . Q^T (B operand; lane (g, n) serves column n,
@@ -515,8 +516,9 @@ __device__ __forceinline__ void mprocess(MState<D, F>& st, const MTile<D, F> (&t
 #pragma unroll
             for (int nb = 0; nb < C::DPL; ++nb) st.acc[nb] *= f;
             st.vr = vmax;
+            st.vinv = 1.0f / vmax;  // vmax > 0 here
         }
-        const float inv = st.vr > 0.0f ? 1.0f / st.vr : 0.0f;
+        const float inv = st.vinv;
 #pragma unroll
         for (int u = 0; u < SLOT; ++u) vrel[u] = vsc[u] * inv;
     }
@@ -830,6 +832,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             st.m = -INFINITY;
             st.l = 0.0f;
             st.vr = 0.0f;
+            st.vinv = 0.0f;
         }
         // the next chunk: prefetch its ids (and a new row's query)
         Seg ng = cg;
