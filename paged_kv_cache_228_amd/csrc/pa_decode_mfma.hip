@@ -806,8 +806,8 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
 
         // Two-slot ring: one slot is computed while the other's loads are in
         // flight. Tiles past the chunk load nothing (zero-byte descriptors)
-        // and all their rows are dead; the loop has no early exit, so the last
-        // step may compute one empty slot.
+        // and all their rows are dead; the loop takes two slots a step, and a
+        // second slot wholly past the chunk is not computed.
         MTile<D, F> ring[2][SLOT];
         float ks[2][SLOT], vs[2][SLOT];
         // a slot's ids are read from LDS one slot ahead of its loads
@@ -857,8 +857,9 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             read_ids(e1, jj + 3 * SLOT);
             load_slot(0, e0, jj + 2 * SLOT);
             __builtin_amdgcn_sched_barrier(0);
-            mslot<D, F, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1], vs[1],
-                               lane, lo_sel, kl);
+            if (jj + SLOT < nloc)  // a slot wholly past the chunk changes nothing
+                mslot<D, F, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1],
+                                   vs[1], lane, lo_sel, kl);
             __builtin_amdgcn_sched_barrier(0);
         }
 
