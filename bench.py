@@ -255,8 +255,9 @@ def main() -> int:
                          "(a known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path is "
-              "single-GPU by design, see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the decode path is "
+              "built and measured on one GPU (one GPU's share of a sharded batch: by sequence "
+              "or by KV head, with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np
