@@ -205,18 +205,25 @@ def config_table(pa, W, torch, np, dev, with_oracle):
 
 def hbm_probe(pa, torch, np, dev):
     """HBM rates for context: the library's streaming-read probe over 4 GiB
-    (the practical read ceiling: the best of 1,024, 2,048 and 4,096
-    workgroups, each the median of 10 calls), torch's sum of the same 4 GiB
-    (bytes read / time) and a 2 GiB device copy (bytes read + written / time);
-    medians of 10."""
+    (the practical read ceiling) and its read-and-write probe (4 GiB read, 2
+    GiB written: the quantizer's mix), each the best of 1,024, 2,048 and
+    4,096 workgroups, each the median of 10 calls; torch's sum of the same 4
+    GiB (bytes read / time) and a 2 GiB device copy (bytes read + written /
+    time); medians of 10."""
     res = {}
     x = torch.ones(1 << 30, dtype=torch.float32, device=dev)
-    best = 0.0
+    best = best_rw = 0.0
+    half = torch.empty(1 << 29, dtype=torch.float32, device=dev)  # 2 GiB
     for groups in (1024, 2048, 4096):
         sink = torch.empty(groups, dtype=torch.int32, device=dev)
         us = per_launch_us(torch, np, lambda i: pa.pa_hbm_read_probe(x, sink), n=10, warm=3)[1]
         best = max(best, round((1 << 32) / us / 1e3, 1))
+        us = per_launch_us(torch, np, lambda i: pa.pa_hbm_rw_probe(x, half, groups), n=10, warm=3)[1]
+        best_rw = max(best_rw, round(3 * (1 << 31) / us / 1e3, 1))
     res["stream_read_gbs"] = best
+    # the quantizer's mix: 4 GiB read, 2 GiB written (bytes read + written / time)
+    res["stream_read2_write1_gbs"] = best_rw
+    del half
     src = torch.ones(1 << 31, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for key, fn, nbytes in (("sum_read_gbs", lambda: x.sum(), 1 << 32),

@@ -295,6 +295,18 @@ int pa_copy_blocks(const void* src_pool, void* dst_pool, int64_t bytes_per_block
  * aligned) or PA_ERR_HIP. */
 int pa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int workgroups, void* stream);
 
+/* Measurement utility: the same streaming read, also writing half as many
+ * bytes (the INT8 quantizer's mix of two bytes read per byte written), so
+ * the quantizer's achieved GB/s can be read next to what the device reaches
+ * for that mix. 16-byte word i of `src` (device, `bytes` bytes) becomes
+ * 8-byte word i of `dst` (device, bytes / 2 bytes, 8-byte aligned): its low
+ * 8 bytes XOR its high 8 bytes. Non-temporal loads and stores, `workgroups`
+ * workgroups of 256 lanes. One asynchronous kernel on `stream`. Returns
+ * PA_OK, PA_ERR_NULL, PA_ERR_SHAPE (bytes or workgroups <= 0),
+ * PA_ERR_UNSUPPORTED (bytes not a multiple of 16, src not 16-byte or dst not
+ * 8-byte aligned) or PA_ERR_HIP. */
+int pa_hbm_rw_probe(const void* src, int64_t bytes, void* dst, int workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

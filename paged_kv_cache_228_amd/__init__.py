@@ -57,6 +57,7 @@ EXPORTED = (
     "pa_internal_fragmentation",
     "pa_copy_blocks",
     "pa_hbm_read_probe",
+    "pa_hbm_rw_probe",
 )
 
 
@@ -123,6 +124,8 @@ def lib() -> C.CDLL:
         L.pa_copy_blocks.restype = i32
         L.pa_hbm_read_probe.argtypes = [p, i64, p, i32, p]
         L.pa_hbm_read_probe.restype = i32
+        L.pa_hbm_rw_probe.argtypes = [p, i64, p, i32, p]
+        L.pa_hbm_rw_probe.restype = i32
         _lib = L
     return _lib
 
@@ -498,11 +501,25 @@ def pa_hbm_read_probe(src, sink, stream=None):
         raise PagedAttentionError("pa_hbm_read_probe", rc)
 
 
+def pa_hbm_rw_probe(src, dst, workgroups, stream=None):
+    """Read the device tensor `src` once and write half as many bytes to the
+    device tensor `dst` (8-byte word i = the two halves of 16-byte word i of
+    src, XORed), over `workgroups` workgroups."""
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes // 2:
+        raise ValueError("dst must hold half of src's bytes")
+    rc = lib().pa_hbm_rw_probe(_ptr(src), nbytes, _ptr(dst), int(workgroups), _stream(src, stream))
+    if rc:
+        raise PagedAttentionError("pa_hbm_rw_probe", rc)
+
+
 __all__ = [
     "LIB_PATH", "EXPORTED", "PagedAttentionError", "lib", "pa_error_string",
     "pa_quantize_kv_int8", "pa_decode_workspace_bytes", "pa_decode_shares",
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
     "pa_append_kv_int8", "pa_evict_select", "pa_quantize_kv_fp8", "pa_paged_decode_fp8",
     "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8", "BlockManager", "pa_internal_fragmentation",
-    "pa_copy_blocks", "pa_hbm_read_probe",
+    "pa_copy_blocks", "pa_hbm_read_probe", "pa_hbm_rw_probe",
 ]

@@ -324,6 +324,21 @@ int pa_hbm_read_probe(const void* src, int64_t bytes, uint32_t* sink, int workgr
     a.src = src;
     a.words = bytes / 16;
     a.sink = sink;
+    a.dst = nullptr;
+    hipError_t e = pa::launch_read_probe(a, workgroups, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e);
+}
+
+int pa_hbm_rw_probe(const void* src, int64_t bytes, void* dst, int workgroups, void* stream)
+{
+    if (!src || !dst) return PA_ERR_NULL;
+    if (bytes <= 0 || workgroups <= 0) return PA_ERR_SHAPE;
+    if (bytes % 16 || !aligned16(src) || (reinterpret_cast<uintptr_t>(dst) & 7u)) return PA_ERR_UNSUPPORTED;
+    pa::ProbeArgs a;
+    a.src = src;
+    a.words = bytes / 16;
+    a.sink = nullptr;
+    a.dst = dst;
     hipError_t e = pa::launch_read_probe(a, workgroups, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : hip_fail(e);
 }

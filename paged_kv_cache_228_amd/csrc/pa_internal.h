@@ -133,7 +133,8 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 struct ProbeArgs {
     const void* src;  // 16-byte aligned
     int64_t words;    // 16-byte words to read
-    uint32_t* sink;   // [workgroups]
+    uint32_t* sink;   // read probe: [workgroups]
+    void* dst;        // read-and-write probe: [words] 8-byte words (NULL: read probe)
 };
 
 hipError_t launch_read_probe(const ProbeArgs& a, int workgroups, hipStream_t st);

@@ -228,3 +228,19 @@ def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypa
 )
 def test_read_probe_rejects_bad_arguments_on_host(args, code):
     assert pa.lib().pa_hbm_read_probe(*args, None) == code
+
+
+@pytest.mark.parametrize(
+    "args, code",
+    [
+        ((None, 1024, FAKE, 4), pa.PA_ERR_NULL),
+        ((FAKE, 1024, None, 4), pa.PA_ERR_NULL),
+        ((FAKE, 0, FAKE, 4), pa.PA_ERR_SHAPE),
+        ((FAKE, 1024, FAKE, 0), pa.PA_ERR_SHAPE),
+        ((FAKE, 1000, FAKE, 4), pa.PA_ERR_UNSUPPORTED),
+        ((FAKE + 8, 1024, FAKE, 4), pa.PA_ERR_UNSUPPORTED),
+        ((FAKE, 1024, FAKE + 4, 4), pa.PA_ERR_UNSUPPORTED),
+    ],
+)
+def test_rw_probe_rejects_bad_arguments_on_host(args, code):
+    assert pa.lib().pa_hbm_rw_probe(*args, None) == code

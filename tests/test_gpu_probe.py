@@ -26,3 +26,17 @@ def test_read_probe_folds_every_word(nbytes, groups):
     assert np.bitwise_xor.reduce(got) == want
     if groups == 1:
         assert got[0] == want
+
+
+@pytest.mark.parametrize("nbytes, groups", [(16, 1), (32768 + 48, 3), ((1 << 22) + 4096, 1024)])
+def test_rw_probe_writes_every_word(nbytes, groups):
+    say(f"read-write probe {nbytes} B, {groups} workgroups")
+    rng = np.random.default_rng(nbytes * 7 + groups)
+    host = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    dst = torch.full((nbytes // 8,), -1, dtype=torch.int32, device=DEV)
+    pa.pa_hbm_rw_probe(src, dst, groups)
+    torch.cuda.synchronize()
+    w = host.reshape(-1, 4)
+    want = np.stack([w[:, 0] ^ w[:, 2], w[:, 1] ^ w[:, 3]], 1).reshape(-1)
+    assert np.array_equal(dst.cpu().numpy().view(np.uint32), want)
