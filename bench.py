@@ -651,6 +651,13 @@ def main() -> int:
         t_cfg = time.time()
         result["configs"] = config_table(pa, W, torch, np, dev, not args.no_cpu_baseline)
         result["hbm_probe"] = hbm_probe(pa, torch, np, dev)
+        # the dominant call against the ceiling the device reaches for its own
+        # traffic mix: reads only (the decodes) or two bytes read per byte
+        # written (the quantizer)
+        key = "stream_read2_write1_gbs" if dom == "quantize" else "stream_read_gbs"
+        ceiling = result["hbm_probe"][key]
+        result["roofline"]["measured_ceiling"] = {
+            "gbs": ceiling, "probe": key, "frac": round(paths[dom]["gbs"] / ceiling, 4)}
         print(f"[bench] configs and probe in {time.time() - t_cfg:.1f}s", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
     return 0
