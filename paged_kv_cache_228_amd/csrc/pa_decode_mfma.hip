@@ -73,10 +73,14 @@ constexpr float kPUnscale = 1.0f / 64.0f;
 #ifndef PA_SLOT_F8
 #define PA_SLOT_F8 2
 #endif
-// Cache-policy bits of the K/V tile loads (2: non-temporal).
+// Cache-policy bits of the K/V tile loads: non-temporal (2) for tiles read
+// once; the default policy (0) for blocks the neighbouring rows of the batch
+// also reference (a shared prefix), which other waves of the same die read
+// at about the same time.
 #ifndef PA_KV_AUX
 #define PA_KV_AUX 2
 #endif
+constexpr int kKvAuxShared = 0;
 // Waves per SIMD the register allocation must leave room for. A ring of two
 // 4-tile fp16 slots needs more than half of the register file, so fp16 is
 // bounded for one wave per SIMD with 32 KiB of loads in flight per wave;
@@ -185,12 +189,12 @@ template <> struct VChunk<16> { typedef u32x4 type; };
 template <> struct VChunk<8> { typedef u32x2 type; };
 template <> struct VChunk<4> { typedef uint32_t type; };
 
-template <int VB>
+template <int VB, int AUX>
 __device__ __forceinline__ typename VChunk<VB>::type vload(rsrc_t r, int off)
 {
-    if constexpr (VB == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_KV_AUX);
-    else if constexpr (VB == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PA_KV_AUX);
-    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, PA_KV_AUX);
+    if constexpr (VB == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    else if constexpr (VB == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
 }
 
 // A tile as loaded: K in tile order (FP8: 8 codes per register pair), V as
@@ -206,7 +210,7 @@ struct MTile {
 // valid == false (past the chunk) or bid < 0 (an id outside the pool, marked
 // when staged) gives a zero-byte descriptor: the loads return zeros and touch
 // no memory, and the scales are 0.
-template <int D, int F>
+template <int D, int F, int AUX>
 __device__ __forceinline__ void mload(MTile<D, F>& t, const DecodeArgs& a, int bid, bool valid,
                                       int kvh, int lane, float& ksc, float& vsc)
 {
@@ -228,13 +232,13 @@ __device__ __forceinline__ void mload(MTile<D, F>& t, const DecodeArgs& a, int b
 #pragma unroll
     for (int c = 0; c < C::KLD; ++c) {
         if constexpr (F == kKvF8)
-            t.k[c] = __builtin_amdgcn_raw_buffer_load_b64(rk, 512 * c + 8 * lane, 0, PA_KV_AUX);
+            t.k[c] = __builtin_amdgcn_raw_buffer_load_b64(rk, 512 * c + 8 * lane, 0, AUX);
         else
-            t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * c + 16 * lane, 0, PA_KV_AUX);
+            t.k[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, 1024 * c + 16 * lane, 0, AUX);
     }
     // V: token 4g+ks, this lane's DPL dims (n * DPL ..)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) t.v[ks] = vload<C::SVB>(rv, (4 * g + ks) * D * C::SEB + n * C::SVB);
+    for (int ks = 0; ks < 4; ++ks) t.v[ks] = vload<C::SVB, AUX>(rv, (4 * g + ks) * D * C::SEB + n * C::SVB);
 }
 
 // K reaches the matrix cores through LDS. A load in operand order (lane =
@@ -702,6 +706,10 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
 {
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
+    // Blocks shared with a neighbouring row are read with the default cache
+    // policy (fp16 only: measured, the per-tile policy branch costs the
+    // INT8 and FP8 kernels more than the caching gains them).
+    constexpr bool kShareAware = F == kKvF16;
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;
@@ -766,12 +774,22 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     // chunk's table entries (and, when it starts a row, that row's query) are
     // loaded while the current chunk is computed, so switching chunks or rows
     // does not wait on memory.
-    auto fetch_ids = [&](const Seg& sg, int c0, int (&tb)[kIdRegs]) {
+    // The chunk's table entries, and for its first 64 blocks the entries the
+    // rows before and after hold at the same positions (-2 where there is no
+    // such row): equal ids mark blocks shared with a neighbouring row.
+    auto fetch_ids = [&](const Seg& sg, int c0, int (&tb)[kIdRegs], int& tp, int& tn) {
         const int nloc = min(sg.nseg - c0, kMaxChunkBlocks);
+        const int64_t at = (int64_t)sg.s * a.max_blocks + sg.j + c0;
 #pragma unroll
         for (int r = 0; r < kIdRegs; ++r) {
             const int i = lane + 64 * r;
-            tb[r] = i < nloc ? a.tables[(int64_t)sg.s * a.max_blocks + sg.j + c0 + i] : -1;
+            tb[r] = i < nloc ? a.tables[at + i] : -1;
+        }
+        if constexpr (kShareAware) {
+            tp = lane < nloc && sg.s > 0 ? a.tables[at - a.max_blocks + lane] : -2;
+            tn = lane < nloc && sg.s + 1 < a.num_seqs ? a.tables[at + a.max_blocks + lane] : -2;
+        } else {
+            tp = tn = -2;
         }
     };
     auto q_row = [&](int row) {
@@ -780,14 +798,24 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     Seg cg;
     take_segment(cg);  // the share holds at least one tile
     int cc0 = 0;
-    int tb[kIdRegs];
+    int tb[kIdRegs], tp, tn;
     QRaw<D, KI8> qraw;
-    fetch_ids(cg, 0, tb);
+    fetch_ids(cg, 0, tb, tp, tn);
     fetch_q<D, KI8>(qraw, q_row(cg.s), qh < group, g);
     QOp<D, KI8> qo;
     MState<D, F> st;
     while (true) {
         const int nloc = min(cg.nseg - cc0, kMaxChunkBlocks);
+        // The run of blocks at the chunk's start that a neighbouring row also
+        // references (within its first 64) is read with the default cache
+        // policy, the rest non-temporally. Only the policy depends on the
+        // neighbours, never the order of the arithmetic.
+        int shared_len = 0;
+        if constexpr (kShareAware) {
+            const uint64_t same =
+                __builtin_amdgcn_ballot_w64(lane < nloc && tb[0] >= 0 && (tb[0] == tp || tb[0] == tn));
+            shared_len = ~same == 0 ? 64 : (int)__builtin_ctzll(~same);
+        }
         const int jb = cg.j + cc0;  // first block of the chunk within the row
         const bool seg_first = cc0 == 0;
         const bool seg_last = cc0 + kMaxChunkBlocks >= cg.nseg;
@@ -815,10 +843,19 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
 #pragma unroll
             for (int u = 0; u < SLOT; ++u) e[u] = mbid[j0_ + u < nloc ? j0_ + u : 0];
         };
+        // issue the loads of ring slot r (blocks j0_ .. j0_ + SLOT - 1 of the
+        // chunk), each with its cache policy (an instruction field, so one
+        // branch per tile, compiled in only where it pays: kShareAware)
         auto load_slot = [&](int r, const int (&e)[SLOT], int j0_) {
 #pragma unroll
-            for (int u = 0; u < SLOT; ++u)
-                mload<D, F>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u], vs[r][u]);
+            for (int u = 0; u < SLOT; ++u) {
+                if (kShareAware && j0_ + u < shared_len)
+                    mload<D, F, kKvAuxShared>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane,
+                                              ks[r][u], vs[r][u]);
+                else
+                    mload<D, F, PA_KV_AUX>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u],
+                                           vs[r][u]);
+            }
         };
         int e0[SLOT], e1[SLOT];
         read_ids(e0, 0);
@@ -843,7 +880,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             nc0 = 0;
         }
         if (have_next) {
-            fetch_ids(ng, nc0, tb);
+            fetch_ids(ng, nc0, tb, tp, tn);
             if (nc0 == 0) fetch_q<D, KI8>(qraw, q_row(ng.s), qh < group, g);
         }
 
