@@ -210,18 +210,26 @@ struct MTile {
 // valid == false (past the chunk) or bid < 0 (an id outside the pool, marked
 // when staged) gives a zero-byte descriptor: the loads return zeros and touch
 // no memory, and the scales are 0.
+template <int D, int F>
+__device__ __forceinline__ void mscales(const DecodeArgs& a, int bid, bool valid, int kvh, float& ksc,
+                                        float& vsc)
+{
+    if constexpr (MCfg<D, F>::SCALED) {  // uniform addresses: one scalar load each
+        const bool in_pool = valid && bid >= 0;
+        const int64_t si = (in_pool ? (int64_t)bid : 0) * a.num_kv_heads + kvh;
+        ksc = in_pool ? a.k_scale[si] : 0.0f;
+        vsc = in_pool ? a.v_scale[si] : 0.0f;
+    }
+}
+
+// The tile's vector loads, with cache-policy bits AUX (its scales: mscales).
 template <int D, int F, int AUX>
 __device__ __forceinline__ void mload(MTile<D, F>& t, const DecodeArgs& a, int bid, bool valid,
-                                      int kvh, int lane, float& ksc, float& vsc)
+                                      int kvh, int lane)
 {
     using C = MCfg<D, F>;
     const bool in_pool = valid && bid >= 0;
     const int64_t b = in_pool ? bid : 0;
-    if constexpr (C::SCALED) {  // uniform addresses: one scalar load each
-        const int64_t si = b * a.num_kv_heads + kvh;
-        ksc = in_pool ? a.k_scale[si] : 0.0f;
-        vsc = in_pool ? a.v_scale[si] : 0.0f;
-    }
     const int64_t off = (b * a.num_kv_heads + kvh) * (int64_t)C::STILE;
     const int bytes = in_pool ? C::STILE : 0;
     const rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + off, bytes);
@@ -707,8 +715,9 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
     // Blocks shared with a neighbouring row are read with the default cache
-    // policy (fp16 only: measured, the per-tile policy branch costs the
-    // INT8 and FP8 kernels more than the caching gains them).
+    // policy: fp16 only. With the per-tile policy branch the INT8 and FP8
+    // kernels ran 30 µs slower on the mixed batch (and 4 to 11 µs slower on
+    // batches with no sharing at all), far more than the caching gains.
     constexpr bool kShareAware = F == kKvF16;
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
@@ -849,12 +858,13 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
         auto load_slot = [&](int r, const int (&e)[SLOT], int j0_) {
 #pragma unroll
             for (int u = 0; u < SLOT; ++u) {
+                const int bid = uniform(e[u]);
+                const bool valid = j0_ + u < nloc;
+                mscales<D, F>(a, bid, valid, kvh, ks[r][u], vs[r][u]);
                 if (kShareAware && j0_ + u < shared_len)
-                    mload<D, F, kKvAuxShared>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane,
-                                              ks[r][u], vs[r][u]);
+                    mload<D, F, kKvAuxShared>(ring[r][u], a, bid, valid, kvh, lane);
                 else
-                    mload<D, F, PA_KV_AUX>(ring[r][u], a, uniform(e[u]), j0_ + u < nloc, kvh, lane, ks[r][u],
-                                           vs[r][u]);
+                    mload<D, F, PA_KV_AUX>(ring[r][u], a, bid, valid, kvh, lane);
             }
         };
         int e0[SLOT], e1[SLOT];
