@@ -261,3 +261,34 @@ def test_many_short_sequences(path, num_seqs):
         tol = TOL_I8
     assert np.max(np.abs(out - ref)) <= tol
     assert not out[ctx == 0].any()
+
+
+def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic():
+    """The fp16 decode reads blocks that a neighbouring row's table also names
+    with another cache policy. Filling every row's table past its last block
+    with its neighbours' ids (entries the decode never reads as tiles) makes
+    the comparison find shared runs where there were none; the outputs must
+    stay bit-identical, as must a shared prefix turned private."""
+    w = workload("mixed_prefix")
+    base = decode_f16(w)
+    t = w.block_tables.copy()
+    nb = (w.context_lens + 15) // 16
+    for s in range(w.num_seqs):
+        src = t[s + 1] if s + 1 < w.num_seqs else t[s - 1]
+        t[s, nb[s]:] = src[nb[s]:]
+    say("shared-block policy: tables filled with the neighbours' ids")
+    assert np.array_equal(decode_f16(w, tables=t).view(np.uint32), base.view(np.uint32))
+    # the second row of every sharing group reads its prefix from private
+    # copies of the same blocks: no shared run left for it
+    k, v, t2 = w.k_pool.copy(), w.v_pool.copy(), w.block_tables.copy()
+    free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
+    used = 0
+    for s in range(1, w.num_seqs, 4):
+        for j in range(min(64, int(nb[s]))):
+            b, f = t2[s, j], free[used]
+            used += 1
+            k[f], v[f] = k[b], v[b]
+            t2[s, j] = f
+    say(f"shared-block policy: {used} prefix blocks made private")
+    assert np.array_equal(decode_f16(w, k_pool=k, v_pool=v, tables=t2).view(np.uint32),
+                          base.view(np.uint32))
