@@ -77,6 +77,12 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is not built; run `python -m paged_kv_cache_228_amd.build`")
+        # torch first: torch ships its own HIP runtime under the same soname, and
+        # the library must bind to that one (loaded first, the system runtime
+        # would sit beside torch's in the process and the two would contend
+        # for the device)
+        import torch  # noqa: F401
+
         L = C.CDLL(LIB_PATH)
         p, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
         L.pa_error_string.argtypes = [i32]

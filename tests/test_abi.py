@@ -194,6 +194,29 @@ def test_workspace_and_share_sizing():
         pa.pa_decode_shares(1, 1, 96, 8)
 
 
+def test_partition_tokens_counts_tokens_per_share_of_the_whole_batch():
+    # A share is a run of one KV head's tiles across sequences, so
+    # partition_tokens is tokens per share of the longest possible batch
+    # (num_seqs x max_blocks_per_seq x 16 tokens), not of one sequence.
+    for S, hkv, d, mb in ((2, 2, 64, 5), (64, 8, 128, 1024), (32, 8, 128, 64)):
+        whole = S * mb * 16
+        for fmt in (pa.KV_F16, pa.KV_INT8, pa.KV_FP8):
+            # covering the whole batch: one share per KV head, no row is cut
+            assert pa.pa_decode_shares(S, hkv, d, mb, 16, whole, fmt) == 1
+            assert pa.pa_decode_shares(S, hkv, d, mb, 16, 4 * whole, fmt) == 1
+            # the longest possible context: still one share per sequence's worth
+            assert pa.pa_decode_shares(S, hkv, d, mb, 16, mb * 16, fmt) == S
+            # the workspace follows the share count: ints + K x 2 x Hq x (d + 2) floats
+            hq = 4 * hkv
+            one = pa.pa_decode_workspace_bytes(S, hq, hkv, d, mb, 16, whole, fmt)
+            ints = ((S + 1 + 1) * 4 + 255) // 256 * 256
+            assert one == ints + 1 * 2 * hq * (d + 2) * 4
+    # the sizing helpers take num_kv_heads: the automatic count spreads one wave
+    # per SIMD (256 CUs x 4 without a device) over the KV heads
+    assert pa.pa_decode_shares(64, 8, 128, 1024) == 128
+    assert pa.pa_decode_shares(64, 4, 128, 1024) == 256
+
+
 def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
     import hashlib
     import json

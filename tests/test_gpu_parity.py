@@ -143,7 +143,9 @@ def test_partition_size_invariance(path):
         outs[p] = run(p)
         assert np.max(np.abs(outs[p] - ref)) <= tol
     for p, o in outs.items():
-        assert np.max(np.abs(o - outs[4096])) <= 1e-5, p
+        diff = float(np.max(np.abs(o - outs[4096])))
+        say(f"  share length {p}: max |out - out(4096)| = {diff:.3e}")
+        assert diff <= 1e-5, p
     assert not outs[0][8].any()  # the empty sequence
 
 
