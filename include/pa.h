@@ -15,7 +15,8 @@
  *    allocates, frees or synchronizes; each call enqueues its kernels on
  *    `stream` (a hipStream_t passed as void*, NULL = the null stream) and
  *    returns without waiting. Calls keep no state and may be issued from
- *    several host threads at once.
+ *    several host threads at once (pa_paged_decode_int8_noalloc aside: its
+ *    workspace is one static device array per GPU, see there).
  *  - K/V pools: [num_blocks][num_kv_heads][block_size][head_dim], row-major;
  *    the 16 x head_dim tile of one (block, KV head) is contiguous. Token t of
  *    sequence s lives in block block_tables[s][t / 16] at slot t % 16
@@ -158,6 +159,29 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          int block_size, int max_blocks_per_seq, int64_t num_blocks,
                          float softmax_scale, int partition_tokens, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* pa_paged_decode_int8 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES bytes that the library holds
+ * on every GPU it runs on until the process ends; the call itself allocates
+ * nothing. All arguments are those of pa_paged_decode_int8 without the
+ * workspace. Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller. Nothing in the array needs clearing between calls (each call
+ * writes what it later reads). Returns PA_ERR_WORKSPACE, before anything is
+ * launched, when the shape needs more workspace than the array holds
+ * (pa_decode_workspace_bytes(..., kv_format 1) > PA_NOALLOC_SCRATCH_BYTES),
+ * PA_ERR_HIP when the array's address cannot be looked up on the current
+ * device, and otherwise what pa_paged_decode_int8 returns. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pa_paged_decode_int8_noalloc(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float* out, int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int max_blocks_per_seq,
+                                 int64_t num_blocks, float softmax_scale, int partition_tokens,
+                                 void* stream);
 
 /* Same as pa_paged_decode_int8 over an FP8 (OCP E4M3) cache produced by
  * pa_quantize_kv_fp8: K and V elements are e4m3(code) * scale of their

@@ -42,6 +42,7 @@ EXPORTED = (
     "pa_decode_shares",
     "pa_paged_decode_f16",
     "pa_paged_decode_int8",
+    "pa_paged_decode_int8_noalloc",
     "pa_paged_decode_fp8",
     "pa_append_kv_f16",
     "pa_append_kv_int8",
@@ -100,6 +101,8 @@ def lib() -> C.CDLL:
         L.pa_paged_decode_f16.restype = i32
         L.pa_paged_decode_int8.argtypes = [p, p, p, p, p] + tail
         L.pa_paged_decode_int8.restype = i32
+        L.pa_paged_decode_int8_noalloc.argtypes = [p, p, p, p, p] + tail[:-3] + [p]
+        L.pa_paged_decode_int8_noalloc.restype = i32
         L.pa_paged_decode_fp8.argtypes = [p, p, p, p, p] + tail
         L.pa_paged_decode_fp8.restype = i32
         app = [p, p, i32, i32, i32, i32, i32, i64, p]
@@ -318,6 +321,33 @@ def pa_paged_decode_int8(q, k_cache, v_cache, k_scale, v_scale, block_tables, co
         raise PagedAttentionError("pa_paged_decode_int8", rc)
 
 
+# Bytes of the static device workspace pa_paged_decode_int8_noalloc uses on every
+# GPU (PA_NOALLOC_SCRATCH_BYTES in pa.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def pa_paged_decode_int8_noalloc(q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                 context_lens, out, softmax_scale, partition_tokens=0,
+                                 stream=None):
+    """pa_paged_decode_int8 with the library's static per-GPU workspace: the call
+    allocates nothing (no workspace argument). Calls on one GPU share that
+    workspace and must not overlap."""
+    import torch
+
+    _need(k_cache, "k_cache", torch.int8, 4)
+    _need(v_cache, "v_cache", torch.int8, 4)
+    _need(k_scale, "k_scale", torch.float32, 2)
+    _need(v_scale, "v_scale", torch.float32, 2)
+    S, hq, hkv, d, bs, mb, nb = _decode_args(q, k_cache, block_tables, context_lens, out)
+    rc = lib().pa_paged_decode_int8_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                            _ptr(out), S, hq, hkv, d, bs, mb, nb,
+                                            float(softmax_scale), int(partition_tokens),
+                                            _stream(q, stream))
+    if rc:
+        raise PagedAttentionError("pa_paged_decode_int8_noalloc", rc)
+
+
 def _append_args(k_new, v_new, k_cache, block_tables, positions):
     import torch
 
@@ -527,5 +557,6 @@ __all__ = [
     "workspace_for", "pa_paged_decode_f16", "pa_paged_decode_int8", "pa_append_kv_f16",
     "pa_append_kv_int8", "pa_evict_select", "pa_quantize_kv_fp8", "pa_paged_decode_fp8",
     "kv_format_of", "KV_F16", "KV_INT8", "KV_FP8", "BlockManager", "pa_internal_fragmentation",
-    "pa_copy_blocks", "pa_hbm_read_probe", "pa_hbm_rw_probe",
+    "pa_copy_blocks", "pa_hbm_read_probe", "pa_hbm_rw_probe", "pa_paged_decode_int8_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]

@@ -282,6 +282,39 @@ int pa_paged_decode_int8(const void* q, const int8_t* k_cache, const int8_t* v_c
                          workspace, workspace_bytes, stream, pa::kKvI8);
 }
 
+int pa_paged_decode_int8_noalloc(const void* q, const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 float* out, int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int max_blocks_per_seq,
+                                 int64_t num_blocks, float softmax_scale, int partition_tokens,
+                                 void* stream)
+{
+    static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::kNoAllocScratchBytes, "one stated maximum");
+    // every host-side check of the workspace variant, and the size limit, before
+    // any HIP call
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens || !out)
+        return PA_ERR_NULL;
+    int rc = check_decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, partition_tokens);
+    if (rc) return rc;
+    if (!std::isfinite(softmax_scale)) return PA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    const long long shares = shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
+                                             partition_tokens, pa::kKvI8);
+    const size_t need = pa::workspace_bytes(num_seqs, num_q_heads, head_dim, (int)shares);
+    if (need > pa::kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+    void* scratch = nullptr;
+    hipError_t e = pa::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    return decode_common(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, out,
+                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, softmax_scale, partition_tokens, scratch,
+                         pa::kNoAllocScratchBytes, stream, pa::kKvI8);
+}
+
 int pa_paged_decode_fp8(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                         const float* k_scale, const float* v_scale, const int32_t* block_tables,
                         const int32_t* context_lens, float* out, int num_seqs, int num_q_heads,

@@ -18,6 +18,8 @@
 // 3. merge: one wave per (sequence, query head) of a cut row combines its
 //    partials (log-sum-exp: M = max m_k, out = sum 2^(m_k - M) acc_k /
 //    sum 2^(m_k - M) l_k); the rows of empty contexts are written as zeros.
+#include <mutex>
+
 #include "pa_internal.h"
 #include "pa_split.h"
 
@@ -130,6 +132,34 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
 }
 
 }  // namespace
+
+// The decode workspace of pa_paged_decode_int8_noalloc: a file-scope device
+// array each GPU holds from the library's load until the process ends. On the
+// host its name stands in for the array and is not a device address, so its
+// per-device address is looked up once per device (with that device current)
+// and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)
 {

@@ -64,6 +64,12 @@ inline size_t workspace_bytes(int S, int Hq, int D, int shares)
 // Offset (in int32) of the share first rows after rows[S + 1].
 __host__ __device__ inline int64_t ws_first_row(int S) { return (int64_t)S + 1; }
 
+// pa_paged_decode_int8_noalloc's workspace: a static device array of this
+// many bytes per GPU (PA_NOALLOC_SCRATCH_BYTES in pa.h), whose address on the
+// current device noalloc_scratch() looks up once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Work split (prefix sums) -> decode waves -> merge of cut rows, all on `st`.
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);
 hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);
