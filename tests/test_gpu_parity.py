@@ -142,10 +142,13 @@ def test_partition_size_invariance(path):
         say(f"partition {path} tokens={p}")
         outs[p] = run(p)
         assert np.max(np.abs(outs[p] - ref)) <= tol
+    # split-K invariance: outputs agree within 1e-6 whatever the share length
+    # (measured: at most 2.4e-7, reduction order and the rounding of P's hi/lo
+    # halves against a different running maximum)
     for p, o in outs.items():
         diff = float(np.max(np.abs(o - outs[4096])))
         say(f"  share length {p}: max |out - out(4096)| = {diff:.3e}")
-        assert diff <= 1e-5, p
+        assert diff <= 1e-6, p
     assert not outs[0][8].any()  # the empty sequence
 
 
