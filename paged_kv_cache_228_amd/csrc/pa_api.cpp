@@ -36,8 +36,12 @@ int num_compute_units()
 // for shares of about that many tokens, sized for the longest possible batch
 // (num_seqs x max_blocks_per_seq blocks). Otherwise one wave per share fills
 // the device once: compute units x decode waves per unit, split over the KV
-// heads, and no share shorter than 8 blocks of that bound. Never more shares
+// heads, and no share shorter than 8 blocks of that bound; for a bound of at
+// most kTinyBound blocks, shares of one block but at most kMergeRound per
+// sequence (the merge kernel's loads in flight per round). Never more shares
 // than the bound has blocks.
+constexpr long long kTinyBound = 64;
+constexpr long long kMergeRound = 8;
 long long shares_per_head(int num_seqs, int num_kv_heads, int head_dim, int max_blocks,
                           int partition_tokens, int fmt)
 {
@@ -49,7 +53,15 @@ long long shares_per_head(int num_seqs, int num_kv_heads, int head_dim, int max_
     } else {
         const long long waves = (long long)num_compute_units() * pa::decode_waves_per_cu(head_dim, fmt);
         k = std::max(1LL, waves / num_kv_heads);
-        k = std::min(k, (bound + 7) / 8);
+        if (bound <= kTinyBound) {
+            // a tiny batch is all latency: shares of one block, so that no wave
+            // walks two rows' segments one after the other, but no more than
+            // kMergeRound per sequence, so that a row's partials are merged in
+            // one round of loads
+            k = std::min(k, std::min(bound, (long long)kMergeRound * num_seqs));
+        } else {
+            k = std::min(k, (bound + 7) / 8);
+        }
     }
     return std::max(1LL, std::min(k, bound));
 }

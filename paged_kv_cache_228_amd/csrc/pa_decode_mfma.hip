@@ -109,6 +109,16 @@ __device__ __forceinline__ uint32_t word(const uint32_t& v, int) { return v; }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The lane's index, computed where it is used: the output and partial
+// addresses of emit() are then formed there instead of being hoisted to the
+// kernel's start and kept in registers across the hot loop (which spilled).
+__device__ __forceinline__ int lane_here()
+{
+    int v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
@@ -430,13 +440,30 @@ __device__ __forceinline__ void make_q(QOp<D, I8>& qo, const QRaw<D, I8>& qr)
     }
 }
 
+// Codes b and b + 1 (b = 0 or 2) of the two tokens whose sign-flipped code
+// words are interleaved in `il` (bytes: token 0's code b, token 1's code b,
+// token 0's code b + 1, token 1's) as two exact fp16 pairs, one per code:
+// each byte goes under the fp16 pattern 0x64xx (a byte permute with a word
+// of 0x64 bytes) and 1152 is subtracted (see code_pair).
+__device__ __forceinline__ uint32_t code_pair_il(uint32_t il, int half)
+{
+    const uint32_t sel = half ? 0x04030402u : 0x04010400u;
+    const uint32_t two = __builtin_amdgcn_perm(0x64646464u, il, sel);
+    const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, two) - bias);
+}
+
 // The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
 template <int D, int F>
 __device__ __forceinline__ uint32_t v_word(const MTile<D, F>& t, int nb, int h)
 {
     if constexpr (F == kKvI8) {
-        return code_pair(word(t.v[2 * h], nb >> 2) ^ 0x80808080u,
-                         word(t.v[2 * h + 1], nb >> 2) ^ 0x80808080u, nb & 3);
+        // the two tokens' sign-flipped code words, interleaved for codes
+        // 4w + 2p and 4w + 2p + 1 (w = nb / 4, p = (nb / 2) % 2)
+        const uint32_t u0 = word(t.v[2 * h], nb >> 2) ^ 0x80808080u;
+        const uint32_t u1 = word(t.v[2 * h + 1], nb >> 2) ^ 0x80808080u;
+        const uint32_t il = __builtin_amdgcn_perm(u1, u0, (nb & 2) ? 0x07030602u : 0x05010400u);
+        return code_pair_il(il, nb & 1);
     } else if constexpr (F == kKvF8) {
         return e4m3_pair2(word(t.v[2 * h], nb >> 2), word(t.v[2 * h + 1], nb >> 2), nb & 3);
     } else {
@@ -594,9 +621,10 @@ __device__ __forceinline__ void mslot(MState<D, F>& st, const MTile<D, F> (&t)[S
 // row, 1: its last) for the merge kernel.
 template <int D, int F>
 __device__ __forceinline__ void emit(MState<D, F>& st, const DecodeArgs& a, int s, int kvh, int group,
-                                     int share, bool cut, int slot, int lane)
+                                     int share, bool cut, int slot)
 {
     using C = MCfg<D, F>;
+    const int lane = lane_here();
     const int g = lane >> 4, n = lane & 15;
     // fold the lo rows (8..15, lane groups 2 and 3) onto the hi rows (0..7,
     // lane groups 0 and 1); the denominator of head n, summed over the four
@@ -914,7 +942,7 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
             const int nb = nblk(cg.s);
             // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
             emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nb,
-                        cg.s == s0 && cg.j == j0 ? 0 : 1, lane);
+                        cg.s == s0 && cg.j == j0 ? 0 : 1);
         }
         if (!have_next) break;
         cg = ng;
