@@ -453,6 +453,45 @@ __device__ __forceinline__ uint32_t code_pair_il(uint32_t il, int half)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, two) - bias);
 }
 
+// The four V operand words of a pair of INT8 tiles for code byte B of word
+// x0..x3 (tile a's tokens 4g..4g+3) and y0..y3 (tile b's): each word is
+// the fp16 pair of two consecutive tokens' codes. The conversion takes the
+// byte straight from its word, sign-extended (sub-dword operand select), so
+// no byte moves and no bias is needed; every int8 value is an fp16 value.
+// All low halves are written before any high half (which keeps the partial
+// register writes apart), and the trailing wait states cover the partial
+// writes' forwarding to the matrix core that reads the words.
+template <int B>
+__device__ __forceinline__ u32x4 i8_vwords(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t y0,
+                                           uint32_t y1, uint32_t y2, uint32_t y3)
+{
+    static_assert(B >= 0 && B < 4, "a byte of a word");
+    uint32_t w0, w1, w2, w3;
+#define PA_SDWA_CVT(DST, SRC, HALF, KEEP) \
+    "v_cvt_f16_i16_sdwa " DST ", sext(" SRC ") dst_sel:" HALF " dst_unused:" KEEP " src0_sel:BYTE_%12\n\t"
+    asm(PA_SDWA_CVT("%0", "%4", "WORD_0", "UNUSED_PAD") PA_SDWA_CVT("%1", "%6", "WORD_0", "UNUSED_PAD")
+        PA_SDWA_CVT("%2", "%8", "WORD_0", "UNUSED_PAD") PA_SDWA_CVT("%3", "%10", "WORD_0", "UNUSED_PAD")
+        PA_SDWA_CVT("%0", "%5", "WORD_1", "UNUSED_PRESERVE") PA_SDWA_CVT("%1", "%7", "WORD_1", "UNUSED_PRESERVE")
+        PA_SDWA_CVT("%2", "%9", "WORD_1", "UNUSED_PRESERVE") PA_SDWA_CVT("%3", "%11", "WORD_1", "UNUSED_PRESERVE")
+        "s_nop 1"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+        : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "v"(y0), "v"(y1), "v"(y2), "v"(y3), "i"(B));
+#undef PA_SDWA_CVT
+    return u32x4{w0, w1, w2, w3};
+}
+
+// i8_vwords for a byte index known after unrolling.
+__device__ __forceinline__ u32x4 i8_vwords_at(int b, uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                              uint32_t y0, uint32_t y1, uint32_t y2, uint32_t y3)
+{
+    switch (b) {
+    case 0: return i8_vwords<0>(x0, x1, x2, x3, y0, y1, y2, y3);
+    case 1: return i8_vwords<1>(x0, x1, x2, x3, y0, y1, y2, y3);
+    case 2: return i8_vwords<2>(x0, x1, x2, x3, y0, y1, y2, y3);
+    default: return i8_vwords<3>(x0, x1, x2, x3, y0, y1, y2, y3);
+    }
+}
+
 // The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
 template <int D, int F>
 __device__ __forceinline__ uint32_t v_word(const MTile<D, F>& t, int nb, int h)
@@ -592,8 +631,15 @@ __device__ __forceinline__ void mprocess(MState<D, F>& st, const MTile<D, F> (&t
         const MTile<D, F>& tb = t[2 * pr + 1];
 #pragma unroll
         for (int nb = 0; nb < C::DPL; ++nb) {
-            u32x4 vw = {v_word<D, F>(ta, nb, 0), v_word<D, F>(ta, nb, 1), v_word<D, F>(tb, nb, 0),
-                        v_word<D, F>(tb, nb, 1)};
+            u32x4 vw;
+            if constexpr (F == kKvI8) {
+                const int w = nb >> 2;
+                vw = i8_vwords_at(nb & 3, word(ta.v[0], w), word(ta.v[1], w), word(ta.v[2], w), word(ta.v[3], w),
+                                  word(tb.v[0], w), word(tb.v[1], w), word(tb.v[2], w), word(tb.v[3], w));
+            } else {
+                vw = u32x4{v_word<D, F>(ta, nb, 0), v_word<D, F>(ta, nb, 1), v_word<D, F>(tb, nb, 0),
+                           v_word<D, F>(tb, nb, 1)};
+            }
             if constexpr (TAIL)
                 vw &= u32x4{vmask[2 * pr][0], vmask[2 * pr][1], vmask[2 * pr + 1][0], vmask[2 * pr + 1][1]};
             st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(h8_t, vw), st.acc[nb],
