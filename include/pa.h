@@ -105,7 +105,8 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
  * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
  * to let the library size one wave per SIMD of the current device over the
  * KV heads (fewer for small batches: at least 8 blocks of that longest batch
- * per share). A share spans sequence boundaries, so this is not a
+ * per share, or, when it has at most 64 blocks, one block per share and at
+ * most 8 shares per sequence). A share spans sequence boundaries, so this is not a
  * per-sequence context partition: a value of at least num_seqs x
  * max_blocks_per_seq x 16 gives one share per KV head, with which no row is
  * cut (no split-K; the merge kernel then only writes the rows of empty
