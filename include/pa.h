@@ -97,10 +97,13 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
                        int head_dim, void* stream);
 
 /* Work split of the decode calls. For every KV head the tiles of all
- * sequences, in sequence order, are cut into equal contiguous shares, one
- * 64-lane wave each; a (sequence, KV head) whose tiles fall in one share is
- * finished by that wave, one cut by share boundaries is completed by a merge
- * kernel from the shares' partial results (log-sum-exp combine).
+ * sequences, in sequence order, are cut into contiguous shares of equal
+ * cost, one 64-lane wave each, where each sequence costs its tiles plus a
+ * few tiles' worth for starting it (spread over its tiles; sequences of equal
+ * length, up to 256 sequences, are cut by tiles alone); a (sequence, KV head)
+ * whose tiles fall in one share is finished by that wave, one cut by share
+ * boundaries is completed by a merge kernel from the shares' partial results
+ * (log-sum-exp combine).
  * partition_tokens: the wanted tokens per share for the longest possible
  * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
  * to let the library size one wave per SIMD of the current device over the

@@ -81,8 +81,9 @@ int check_decode_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head
     if (group < 1 || group > pa::kMaxGroup) return PA_ERR_UNSUPPORTED;
     if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
     if ((long long)max_blocks_per_seq * pa::kBlockTokens > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
-    // tile prefix sums are int32; one workgroup per (share, KV head)
-    if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    // tile and cost prefix sums are int32; one workgroup per (share, KV head)
+    if ((long long)num_seqs * (max_blocks_per_seq + pa::kMaxRowCost) > 0x7fffffffLL)
+        return PA_ERR_UNSUPPORTED;
     for (int fmt = pa::kKvF16; fmt <= pa::kKvF8; ++fmt)
         if (shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq, partition_tokens, fmt) *
                 num_kv_heads > 0x7fffffffLL)
@@ -131,6 +132,7 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     a.num_kv_heads = num_kv_heads;
     a.max_blocks = max_blocks_per_seq;
     a.shares = shares;
+    a.row_cost = pa::decode_row_cost(head_dim, fmt);
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, fmt,
                                      static_cast<hipStream_t>(stream));
@@ -248,7 +250,8 @@ int pa_decode_shares(int num_seqs, int num_kv_heads, int head_dim, int max_block
     if (block_size != pa::kBlockTokens) return PA_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (kv_format < pa::kKvF16 || kv_format > pa::kKvF8) return PA_ERR_UNSUPPORTED;
-    if ((long long)num_seqs * max_blocks_per_seq > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+    if ((long long)num_seqs * (max_blocks_per_seq + pa::kMaxRowCost) > 0x7fffffffLL)
+        return PA_ERR_UNSUPPORTED;
     return (int)std::min(shares_per_head(num_seqs, num_kv_heads, head_dim, max_blocks_per_seq,
                                          partition_tokens, kv_format),
                          0x7fffffffLL);

@@ -29,40 +29,63 @@ namespace {
 __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a)
 {
     const int t = threadIdx.x;
-    __shared__ int wsum[kPrepThreads / 64];
-    __shared__ int carry_s;
+    __shared__ int wsum[2][kPrepThreads / 64];
+    __shared__ int carry_s[2];
     const int lane = t & 63, w = t >> 6;
-    int carry = 0;
+    int32_t* costs = a.rows + ws_costs(a.num_seqs);
+    int carry = 0, ccarry = 0;  // tiles and cost of the rows so far
     for (int base = 0; base < a.num_seqs; base += kPrepThreads) {
         const int s = base + t;
         const int nb = s < a.num_seqs ? clamp_blocks(a.ctx[s], a.max_blocks) : 0;
-        // inclusive scan within the wave, then across the waves
-        int x = nb;
+        const int rc = (int)row_cost_of(nb, a.row_cost);
+        // inclusive scans within the wave, then across the waves
+        int x = nb, y = rc;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(x, d, 64);
-            if (lane >= d) x += y;
+            const int xu = __shfl_up(x, d, 64), yu = __shfl_up(y, d, 64);
+            if (lane >= d) {
+                x += xu;
+                y += yu;
+            }
         }
-        if (lane == 63) wsum[w] = x;
+        if (lane == 63) {
+            wsum[0][w] = x;
+            wsum[1][w] = y;
+        }
         __syncthreads();
-        int before = carry;
-        for (int i = 0; i < w; ++i) before += wsum[i];
-        if (s < a.num_seqs) a.rows[s] = before + x - nb;
-        if (t == kPrepThreads - 1) carry_s = before + x;
+        int before = carry, cbefore = ccarry;
+        for (int i = 0; i < w; ++i) {
+            before += wsum[0][i];
+            cbefore += wsum[1][i];
+        }
+        if (s < a.num_seqs) {
+            a.rows[s] = before + x - nb;
+            costs[s] = cbefore + y - rc;
+        }
+        if (t == kPrepThreads - 1) {
+            carry_s[0] = before + x;
+            carry_s[1] = cbefore + y;
+        }
         __syncthreads();
-        carry = carry_s;
+        carry = carry_s[0];
+        ccarry = carry_s[1];
         __syncthreads();
     }
-    if (t == 0) a.rows[a.num_seqs] = carry;
-    __syncthreads();  // rows[] complete for this workgroup
+    if (t == 0) {
+        a.rows[a.num_seqs] = carry;
+        costs[a.num_seqs] = ccarry;
+    }
+    __syncthreads();  // rows[] and costs[] complete for this workgroup
 
-    const int64_t T = carry, K = a.shares;
+    // the row holding share k's first tile is the row whose cost range holds
+    // b_k (none when no sequence has a tile)
+    const int64_t Q = ccarry, K = a.shares;
+    if (Q == 0) return;
     int32_t* first_row = a.rows + ws_first_row(a.num_seqs);
     for (int s = t; s < a.num_seqs; s += kPrepThreads) {
-        const int64_t r0 = a.rows[s], r1 = a.rows[s + 1];
-        // shares whose first tile lies in [r0, r1)
-        const int64_t k1 = min(first_share_at(r1, T, K), K);
-        for (int64_t k = first_share_at(r0, T, K); k < k1; ++k) first_row[k] = s;
+        const int64_t c0 = costs[s], c1 = costs[s + 1];
+        const int64_t k1 = min(first_share_at(c1, Q, K), K);
+        for (int64_t k = first_share_at(c0, Q, K); k < k1; ++k) first_row[k] = s;
     }
 }
 
@@ -73,24 +96,42 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
 {
     const int hq = blockIdx.x, s = blockIdx.y;
     const int lane = threadIdx.x;
-    const int64_t r0 = a.rows[s], r1 = a.rows[s + 1], T = a.rows[a.num_seqs], K = a.shares;
+    const int32_t* costs = a.rows + ws_costs(a.num_seqs);
+    const int64_t nb = a.rows[s + 1] - a.rows[s];
+    const int64_t c0 = costs[s], c1 = costs[s + 1], Q = costs[a.num_seqs], K = a.shares;
     float* o = a.out + ((int64_t)s * a.num_q_heads + hq) * D;
     constexpr int NC = D / 64;
-    if (r1 == r0) {  // empty context: a zero row
+    if (nb == 0) {  // empty context: a zero row
 #pragma unroll
         for (int c = 0; c < NC; ++c) o[lane + 64 * c] = 0.0f;
         return;
     }
-    // the first and the last share holding the row's tiles
-    const int64_t kf = share_of(r0, T, K), kl = share_of(r1 - 1, T, K);
+    // the shares holding the row's first and last tile (pa_split.h: the
+    // shares of the last units of their cost intervals)
+    const int64_t R = c1 - c0;  // nb + c, below 2^31 like every row's tile count
+    const int64_t kf = share_of(c0 + (int64_t)((uint32_t)R / (uint32_t)nb) - 1, Q, K);
+    const int64_t kl = share_of(c1 - 1, Q, K);
     if (kf == kl) return;  // finished by its one share
     const int kvh = hq / group, qi = hq - kvh * group;
     const int64_t nslot = K * a.num_kv_heads * 2 * group;
-    // partial entry of share k (0 when it holds no tile of the row)
+    // Partial entry of share k, and whether share k holds tiles of the row:
+    // the first does; a later one from the tile at b_k up to the one before
+    // the tile at b_{k+1}, if that is another tile, or to the row's end. No
+    // share is empty when each spans at least the widest tile (1 + c units).
+    const bool none_empty = Q >= K * (1 + (int64_t)a.row_cost);
     auto entry = [&](int64_t k, bool& live) {
-        live = k <= kl && (T >= K || !share_empty(k, T, K));
-        // the first share holds the row in its last slot unless the row starts its range
-        const int slot = (k == kf && k * T / K < r0) ? 1 : 0;
+        if (k > kl) {
+            live = false;
+        } else if (k == kf || none_empty) {
+            live = true;
+        } else {
+            const int64_t b1 = share_start(k + 1, Q, K);
+            live = b1 >= c1 || tile_at_cost(b1 - c0, nb, R) != tile_at_cost(share_start(k, Q, K) - c0, nb, R);
+        }
+        // slot 1 holds the row in the share holding its first tile (the row
+        // is that share's last segment), slot 0 in every later share (the
+        // row is that share's first segment)
+        const int slot = k == kf ? 1 : 0;
         return ((k * a.num_kv_heads + kvh) * 2 + slot) * group + qi;
     };
     // kMergeShares shares per round, their m, l and acc loads all in flight

@@ -663,8 +663,9 @@ __device__ __forceinline__ void mslot(MState<D, F>& st, const MTile<D, F> (&t)[S
 
 // The end of one (sequence, KV head) segment of a share. If the segment is
 // the row's whole context its query heads' outputs are written; otherwise its
-// partial (acc, m, l) goes to slot `slot` of the share (0: the share's first
-// row, 1: its last) for the merge kernel.
+// partial (acc, m, l) goes to slot `slot` of the share for the merge kernel
+// (1: the row started in this share, which holds its first tile; 0: the row
+// started in an earlier share).
 template <int D, int F>
 __device__ __forceinline__ void emit(MState<D, F>& st, const DecodeArgs& a, int s, int kvh, int group,
                                      int share, bool cut, int slot)
@@ -714,10 +715,12 @@ __device__ __forceinline__ void emit(MState<D, F>& st, const DecodeArgs& a, int 
 
 // This wave's place in the work split (pa_split.h): its share's tile range
 // [p0, p1) of the KV head's T tiles and the row s0 holding tile p0, whose
-// first tile is rs0. Up to kScanSeqs sequences the wave scans the context
-// lengths itself (four per lane) and the grid's first wave stores the prefix
-// sums rows[0..S] for the merge kernel; beyond that the prep kernel has stored
-// them, with the first row of every share.
+// first tile is rs0. The share's ends come from the cost line: b = k Q / K
+// lies in one row's cost range, and p is that row's first tile plus the
+// tile whose interval holds b. Up to kScanSeqs sequences the wave scans the
+// context lengths itself (four per lane) into tile and cost prefix sums, and
+// the grid's first wave stores them for the merge kernel; beyond that the
+// prep kernel has stored them, with the row holding every share's first tile.
 struct ShareLoc {
     int64_t p0, p1;
     int s0, rs0;
@@ -727,24 +730,39 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
     static_assert(kScanSeqs == 4 * 64, "four sequences per lane");
     const int S = a.num_seqs;
     const int64_t K = a.shares;
+    const int32_t* costs = a.rows + ws_costs(S);
     ShareLoc r;
     if (S > kScanSeqs) {
-        const int64_t T = a.rows[S];
-        r.p0 = share * T / K;
-        r.p1 = (share + 1) * T / K;
-        r.s0 = r.p0 < r.p1 ? a.rows[ws_first_row(S) + share] : 0;
+        const int64_t T = a.rows[S], Q = costs[S];
+        const int64_t b0 = share_start(share, Q, K), b1 = share_start(share + 1, Q, K);
+        // the tile whose cost interval holds b, through the row the prep
+        // kernel found for it
+        auto tile_at = [&](int row, int64_t b) {
+            const int64_t c0 = costs[row], rt = a.rows[row];
+            const int64_t nb = a.rows[row + 1] - rt;
+            return rt + tile_at_cost(b - c0, nb, costs[row + 1] - c0);
+        };
+        r.p0 = r.p1 = T;
+        r.s0 = r.rs0 = 0;
+        if (Q == 0) return r;  // no sequence has a tile (and the prep kernel stored no rows)
+        const int32_t* first_row = a.rows + ws_first_row(S);
+        r.s0 = first_row[share];
+        r.p0 = tile_at(r.s0, b0);
+        if (share + 1 < K) r.p1 = tile_at(first_row[share + 1], b1);
         r.rs0 = a.rows[r.s0];
         return r;
     }
-    int nb[4], ex[4];
+    int nb[4], ex[4], exc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int s = 64 * u + lane;
         nb[u] = s < S ? clamp_blocks(a.ctx[s], a.max_blocks) : 0;
     }
+    // exclusive tile prefix sums (a 64-lane scan per 64 rows)
     int carry = 0;
+    uint64_t live[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // exclusive prefix sums, 64 rows at a time
+    for (int u = 0; u < 4; ++u) {
         int x = nb[u];
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -752,30 +770,92 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
             if (lane >= d) x += y;
         }
         ex[u] = carry + x - nb[u];
-        carry += __shfl(x, 63, 64);
+        carry += __builtin_amdgcn_readlane(x, 63);
+        live[u] = __builtin_amdgcn_ballot_w64(nb[u] > 0);
     }
-    if (blockIdx.x == 0) {
+    // The row cost, unless every non-empty row has as many tiles as the first:
+    // rows of equal length take the plain split (cost 0), which cuts them the
+    // same way wherever its shares fall on row boundaries, with less
+    // arithmetic here.
+    int nb_first = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (64 * u + lane < S) a.rows[64 * u + lane] = ex[u];
-        if (lane == 0) a.rows[S] = carry;
-    }
-    const int64_t T = uniform(carry);
-    r.p0 = share * T / K;
-    r.p1 = (share + 1) * T / K;
+    for (int u = 3; u >= 0; --u)
+        if (live[u] != 0) nb_first = __builtin_amdgcn_readlane(nb[u], __builtin_ctzll(live[u]));
+    bool equal = true;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) equal = equal && __builtin_amdgcn_ballot_w64(nb[u] > 0 && nb[u] != nb_first) == 0;
+    const int c = equal ? 0 : a.row_cost;
     r.s0 = 0;
     r.rs0 = 0;
+    if (c == 0) {  // tiles and costs coincide: share k is [k T / K, (k + 1) T / K)
+        if (blockIdx.x == 0) {
+            int32_t* costs_w = a.rows + ws_costs(S);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // the one row with ex <= p0 < ex + nb, if p0 < T
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[u] > 0 && ex[u] <= r.p0 && r.p0 < ex[u] + nb[u]);
-        if (hit != 0) {
-            const int l = __builtin_ctzll(hit);
-            r.s0 = 64 * u + l;
-            r.rs0 = __shfl(ex[u], l, 64);
+            for (int u = 0; u < 4; ++u)
+                if (64 * u + lane < S) a.rows[64 * u + lane] = costs_w[64 * u + lane] = ex[u];
+            if (lane == 0) a.rows[S] = costs_w[S] = carry;
+        }
+        const int64_t T = uniform(carry);
+        r.p0 = share * T / K;
+        r.p1 = (share + 1) * T / K;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[u] > 0 && ex[u] <= r.p0 && r.p0 < ex[u] + nb[u]);
+            if (hit != 0) {
+                const int l = __builtin_ctzll(hit);
+                r.s0 = 64 * u + l;
+                r.rs0 = __builtin_amdgcn_readlane(ex[u], l);
+            }
+        }
+        return r;
+    }
+    // the cost prefix adds c per non-empty row before, counted from the ballots
+    int rows_before = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(live[u] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)live[u], 0));
+        exc[u] = ex[u] + c * (rows_before + before);
+        rows_before += __builtin_popcountll(live[u]);
+    }
+    if (blockIdx.x == 0) {
+        int32_t* costs_w = a.rows + ws_costs(S);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (64 * u + lane < S) {
+                a.rows[64 * u + lane] = ex[u];
+                costs_w[64 * u + lane] = exc[u];
+            }
+        if (lane == 0) {
+            a.rows[S] = carry;
+            costs_w[S] = carry + c * rows_before;
         }
     }
-    r.s0 = uniform(r.s0);
-    r.rs0 = uniform(r.rs0);
+    const int64_t T = uniform(carry), Q = T + (int64_t)c * uniform(rows_before);
+    // the tiles whose cost intervals hold b0 and b1 (when below Q), each
+    // through the one row with exc <= b < exc + nb + c, found in one pass
+    const int64_t b0 = share_start(share, Q, K), b1 = share_start(share + 1, Q, K);
+    r.p0 = T;
+    r.p1 = T;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const bool has = nb[u] > 0;
+        const uint64_t hit0 = __builtin_amdgcn_ballot_w64(has && exc[u] <= b0 && b0 < exc[u] + nb[u] + c);
+        const uint64_t hit1 = __builtin_amdgcn_ballot_w64(has && exc[u] <= b1 && b1 < exc[u] + nb[u] + c);
+        if (hit0 != 0) {
+            const int l = __builtin_ctzll(hit0);
+            const int n = __builtin_amdgcn_readlane(nb[u], l);
+            r.s0 = 64 * u + l;
+            r.rs0 = __builtin_amdgcn_readlane(ex[u], l);
+            r.p0 = r.rs0 + tile_at_cost(b0 - __builtin_amdgcn_readlane(exc[u], l), n, n + c);
+        }
+        if (hit1 != 0) {
+            const int l = __builtin_ctzll(hit1);
+            const int n = __builtin_amdgcn_readlane(nb[u], l);
+            r.p1 = __builtin_amdgcn_readlane(ex[u], l) +
+                   tile_at_cost(b1 - __builtin_amdgcn_readlane(exc[u], l), n, n + c);
+        }
+    }
     return r;
 }
 
@@ -986,9 +1066,11 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
 
         if (seg_last) {
             const int nb = nblk(cg.s);
-            // slot 0: the share's first segment (row s0 from block j0), slot 1: its last
-            emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nb,
-                        cg.s == s0 && cg.j == j0 ? 0 : 1);
+            // slot 1: a segment from its row's first block (the row goes on
+            // past this share: it is the share's last segment, and this share
+            // holds the row's first tile); slot 0: one from inside its row
+            // (the share's first segment)
+            emit<D, F>(st, a, cg.s, kvh, group, share, cg.j > 0 || cg.j + cg.nseg < nb, cg.j == 0 ? 1 : 0);
         }
         if (!have_next) break;
         cg = ng;
@@ -1006,6 +1088,15 @@ hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
 }
 
 }  // namespace
+
+int decode_row_cost(int, int fmt)
+{
+    // What a wave spends on each row it starts (the table staging, the ring
+    // filling again, the query and the epilogue), in tiles of streaming: per-
+    // wave clock stamps put it near 3 us per row touched against 0.7 us per
+    // INT8 tile; fp16 tiles take twice as long to stream.
+    return fmt == kKvF16 ? 3 : 4;
+}
 
 int decode_waves_per_cu(int, int)
 {

@@ -45,24 +45,30 @@ struct DecodeArgs {
     int num_kv_heads;
     int max_blocks;         // table row length
     int shares;             // shares per KV head
+    int row_cost;           // the work split's cost of starting a row, in tiles (pa_split.h)
     float scale_log2;       // softmax_scale * log2(e)
 };
 
-// Workspace, int32 part: tile prefix sums rows[S + 1]; the first row of each
-// share [shares] (written only when S > kScanSeqs); padded to 256 bytes. Then
+// Workspace, int32 part: tile prefix sums rows[S + 1]; cost prefix sums
+// costs[S + 1] (pa_split.h); the row holding the first tile of each share
+// [shares] (written only when S > kScanSeqs); padded to 256 bytes. Then
 // fp32 partials: acc [shares][Hkv][2][G][D], then m and l, each
-// [shares][Hkv][2][G]; slot 0 of a share holds its first row if that row is
-// cut, slot 1 its last.
+// [shares][Hkv][2][G]; slot 1 of a share holds a cut row whose first tile
+// the share holds (the row is the share's last segment), slot 0 a cut row
+// that began in an earlier share (the share's first segment).
 inline size_t workspace_int_bytes(int S, int shares)
 {
-    return ((size_t)((size_t)S + 1 + shares) * 4 + 255) & ~(size_t)255;
+    return ((size_t)(2 * ((size_t)S + 1) + shares) * 4 + 255) & ~(size_t)255;
 }
 inline size_t workspace_bytes(int S, int Hq, int D, int shares)
 {
     return workspace_int_bytes(S, shares) + (size_t)shares * 2 * Hq * (size_t)(D + 2) * 4;
 }
-// Offset (in int32) of the share first rows after rows[S + 1].
-__host__ __device__ inline int64_t ws_first_row(int S) { return (int64_t)S + 1; }
+// Offsets (in int32) of the cost prefix sums and of the share first rows.
+__host__ __device__ inline int64_t ws_costs(int S) { return (int64_t)S + 1; }
+__host__ __device__ inline int64_t ws_first_row(int S) { return 2 * ((int64_t)S + 1); }
+// Largest row cost of the work split (decode_row_cost), for the size checks.
+constexpr int kMaxRowCost = 8;
 
 // pa_paged_decode_int8_noalloc's workspace: a static device array of this
 // many bytes per GPU (PA_NOALLOC_SCRATCH_BYTES in pa.h), whose address on the
@@ -75,6 +81,8 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, 
 hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st);
 // Decode waves each compute unit holds at once for this configuration.
 int decode_waves_per_cu(int head_dim, int fmt);
+// The work split's row cost, in tiles, for this configuration (0..kMaxRowCost).
+int decode_row_cost(int head_dim, int fmt);
 
 struct QuantArgs {
     const uint16_t* k;

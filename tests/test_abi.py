@@ -170,10 +170,10 @@ def test_workspace_and_share_sizing():
     # Without a device to ask, the library sizes for 256 compute units.
     # A tiny batch: at most one share per 8 blocks of the 2 x 5-block bound.
     assert pa.pa_decode_shares(2, 2, 64, 5) == 10  # a tiny bound: one block per share
-    # int32 prefix sums [S + 1], share first rows [K], padded to 256 B; then
-    # the partials: K x 2 slots x Hq x (D + 2) floats
+    # int32 tile and cost prefix sums [S + 1] each, share first rows [K],
+    # padded to 256 B; then the partials: K x 2 slots x Hq x (D + 2) floats
     def ints(S, K, hkv):
-        return ((S + 1 + K) * 4 + 255) // 256 * 256
+        return ((2 * (S + 1) + K) * 4 + 255) // 256 * 256
 
     assert pa.pa_decode_workspace_bytes(2, 4, 2, 64, 5) == ints(2, 10, 2) + 10 * 2 * 4 * 66 * 4
     # the mixed batch's shape: one share per wave, one wave per SIMD (256 CUs x
@@ -209,7 +209,7 @@ def test_partition_tokens_counts_tokens_per_share_of_the_whole_batch():
             # the workspace follows the share count: ints + K x 2 x Hq x (d + 2) floats
             hq = 4 * hkv
             one = pa.pa_decode_workspace_bytes(S, hq, hkv, d, mb, 16, whole, fmt)
-            ints = ((S + 1 + 1) * 4 + 255) // 256 * 256
+            ints = ((2 * (S + 1) + 1) * 4 + 255) // 256 * 256
             assert one == ints + 1 * 2 * hq * (d + 2) * 4
     # the sizing helpers take num_kv_heads: the automatic count spreads one wave
     # per SIMD (256 CUs x 4 without a device) over the KV heads

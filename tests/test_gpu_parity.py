@@ -268,6 +268,23 @@ def test_many_short_sequences(path, num_seqs):
     assert not out[ctx == 0].any()
 
 
+@pytest.mark.parametrize("path", ["f16", "int8"])
+@pytest.mark.parametrize("num_seqs", [8, 257])
+def test_every_context_empty(path, num_seqs):
+    # no tile at all: the work split is empty (with 257 sequences the prep
+    # kernel finds no share a first row), every row is zeros
+    ctx = np.zeros(num_seqs, dtype=np.int64)
+    w = W.build("empty", 705, ctx, 4, 2, 64, num_blocks=4)
+    say(f"every context empty {path} S={num_seqs}")
+    if path == "f16":
+        out = decode_f16(w)
+    else:
+        kc, ks = oracle.quantize_kv_int8(w.k_pool)
+        vc, vs = oracle.quantize_kv_int8(w.v_pool)
+        out = decode_int8(w, kc, vc, ks, vs)
+    assert out.shape == (num_seqs, 4, 64) and not out.any()
+
+
 def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic():
     """The fp16 decode reads blocks that a neighbouring row's table also names
     with another cache policy. Filling every row's table past its last block
