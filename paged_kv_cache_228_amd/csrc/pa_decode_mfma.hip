@@ -1094,8 +1094,10 @@ int decode_row_cost(int, int fmt)
     // What a wave spends on each row it starts (the table staging, the ring
     // filling again, the query and the epilogue), in tiles of streaming: per-
     // wave clock stamps put it near 3 us per row touched against 0.7 us per
-    // INT8 tile; fp16 tiles take twice as long to stream.
-    return fmt == kKvF16 ? 3 : 4;
+    // INT8 tile, and a sweep of the mixed-length batch was fastest from 8 to
+    // 12 for the one-byte caches (each share then also ends nearer the die
+    // mean); fp16 tiles take twice as long to stream and were flat from 0 to 5.
+    return fmt == kKvF16 ? 3 : 8;
 }
 
 int decode_waves_per_cu(int, int)

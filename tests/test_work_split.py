@@ -2,7 +2,7 @@
 
 Every KV head's tiles (all sequences in order, ceil(ctx / 16) per sequence)
 lie on a cost line: a row of nb > 0 tiles costs R = nb + c (c, the row cost,
-is 3 tiles for fp16 and 4 for INT8 and FP8), spread over its tiles, so tile j
+is 3 tiles for fp16 and 8 for INT8 and FP8), spread over its tiles, so tile j
 of the row covers [C + j R / nb, C + (j + 1) R / nb) with C the cost of the
 rows before it (integer division); up to 256 sequences, rows that all have
 the same length take c = 0. The total cost Q is cut at
@@ -177,7 +177,7 @@ def walk(ctxs, K, max_blocks, c):
     return shares
 
 
-@pytest.mark.parametrize("c", [0, 3, 4])
+@pytest.mark.parametrize("c", [0, 3, 4, 8])
 @pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 13, 64, 300])
 def test_random_batches(K, c):
     rng = random.Random(K * 10 + c)
@@ -187,7 +187,7 @@ def test_random_batches(K, c):
         walk(ctxs, K, mb, c)
 
 
-@pytest.mark.parametrize("c", [0, 3, 4])
+@pytest.mark.parametrize("c", [0, 3, 4, 8])
 def test_edge_batches(c):
     walk([0, 0, 0], 4, 8, c)          # nothing to do
     walk([5], 1, 1, c)                # one tile, one share
@@ -206,7 +206,7 @@ def test_equal_rows_keep_the_plain_split():
     # sequences, where the prep kernel keeps the row cost for equal rows too)
     for S, nb, K in ((32, 64, 128), (64, 128, 128), (8, 32, 32), (4, 16, 16), (300, 8, 600)):
         plain = walk([16 * nb] * S, K, nb, 0)
-        for c in (3, 4):
+        for c in (3, 4, 8):
             assert walk([16 * nb] * S, K, nb, c) == plain
 
 
@@ -214,7 +214,7 @@ def test_row_cost_moves_tiles_off_shares_that_start_many_rows():
     # short rows next to a long one: with a row cost, the shares over the
     # short rows hold fewer tiles than those inside the long row
     ctxs = [16 * 4] * 24 + [16 * 96]
-    sh = walk(ctxs, 8, 96, 4)
+    sh = walk(ctxs, 8, 96, 8)
     lengths = [p1 - p0 for p0, p1 in sh]
     assert lengths[0] < lengths[-1]
     assert walk(ctxs, 8, 96, 0) == [(k * 192 // 8, (k + 1) * 192 // 8) for k in range(8)]
