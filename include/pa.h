@@ -100,7 +100,8 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
  * sequences, in sequence order, are cut into contiguous shares of equal
  * cost, one 64-lane wave each, where each sequence costs its tiles plus a
  * few tiles' worth for starting it (spread over its tiles; sequences of equal
- * length, up to 256 sequences, are cut by tiles alone); a (sequence, KV head)
+ * length, up to 256 sequences, and batches of at most 64 possible blocks per
+ * KV head are cut by tiles alone); a (sequence, KV head)
  * whose tiles fall in one share is finished by that wave, one cut by share
  * boundaries is completed by a merge kernel from the shares' partial results
  * (log-sum-exp combine).

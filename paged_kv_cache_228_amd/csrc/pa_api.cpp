@@ -132,7 +132,9 @@ int decode_common(const void* q, const void* k, const void* v, const float* ks, 
     a.num_kv_heads = num_kv_heads;
     a.max_blocks = max_blocks_per_seq;
     a.shares = shares;
-    a.row_cost = pa::decode_row_cost(head_dim, fmt);
+    // batches of at most kTinyBound possible tiles per KV head keep the plain
+    // split, whose one-tile shares then start no second row
+    a.row_cost = (long long)num_seqs * max_blocks_per_seq <= kTinyBound ? 0 : pa::decode_row_cost(head_dim, fmt);
     a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
     hipError_t e = pa::launch_decode(a, head_dim, num_q_heads / num_kv_heads, fmt,
                                      static_cast<hipStream_t>(stream));

@@ -97,8 +97,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
     const int hq = blockIdx.x, s = blockIdx.y;
     const int lane = threadIdx.x;
     const int32_t* costs = a.rows + ws_costs(a.num_seqs);
-    const int64_t nb = a.rows[s + 1] - a.rows[s];
-    const int64_t c0 = costs[s], c1 = costs[s + 1], Q = costs[a.num_seqs], K = a.shares;
+    const int32_t r0 = a.rows[s], r1 = a.rows[s + 1], cs0 = costs[s], cs1 = costs[s + 1],
+                  cq = costs[a.num_seqs];
+    // these scalar loads (and the arguments used later) in flight together:
+    // one memory round trip, not one per use
+    asm volatile("" ::"s"(r0), "s"(r1), "s"(cs0), "s"(cs1), "s"(cq), "s"(a.shares), "s"(a.num_kv_heads),
+                 "s"(a.part), "s"(group));
+    const int64_t nb = r1 - r0;
+    const int64_t c0 = cs0, c1 = cs1, Q = cq, K = a.shares;
     float* o = a.out + ((int64_t)s * a.num_q_heads + hq) * D;
     constexpr int NC = D / 64;
     if (nb == 0) {  // empty context: a zero row
@@ -117,53 +123,64 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int grou
     // Partial entry of share k, and whether share k holds tiles of the row:
     // the first does; a later one from the tile at b_k up to the one before
     // the tile at b_{k+1}, if that is another tile, or to the row's end. No
-    // share is empty when each spans at least the widest tile (1 + c units).
-    const bool none_empty = Q >= K * (1 + (int64_t)a.row_cost);
-    auto entry = [&](int64_t k, bool& live) {
-        if (k > kl) {
-            live = false;
-        } else if (k == kf || none_empty) {
-            live = true;
-        } else {
-            const int64_t b1 = share_start(k + 1, Q, K);
-            live = b1 >= c1 || tile_at_cost(b1 - c0, nb, R) != tile_at_cost(share_start(k, Q, K) - c0, nb, R);
+    // share is empty when each spans at least the widest tile (1 + c units,
+    // c the row cost the split used: R - nb, the same for every row of the
+    // call, and 0 for rows of equal length); with c = 0 a tile is one unit.
+    const int64_t c = R - nb;
+    const bool none_empty = Q >= K * (1 + c);
+    // kMergeShares shares per round: lane u (mod kMergeShares) finds whether
+    // share k0 + u holds tiles of the row and where its partial is, so the
+    // shares' tests run side by side and every load of the round (m, l and
+    // acc of each share) is in flight together; the combine then takes the
+    // shares in order, as one wave-uniform sum (rows rarely span more than
+    // one round). Across rounds a running maximum M rescales what has been
+    // summed (the log-sum-exp combine, one round at a time).
+    const int u = lane & (kMergeShares - 1);
+    float num[NC] = {};
+    float den = 0.0f, M = -INFINITY;
+    for (int64_t k0 = kf; k0 <= kl; k0 += kMergeShares) {
+        const int64_t k = k0 + u;
+        bool live = k <= kl;
+        if (live && k != kf && !none_empty) {
+            const int64_t b0 = share_start(k, Q, K), b1 = share_start(k + 1, Q, K);
+            live = b1 >= c1 ||
+                   (c == 0 ? b1 != b0 : tile_at_cost(b1 - c0, nb, R) != tile_at_cost(b0 - c0, nb, R));
         }
         // slot 1 holds the row in the share holding its first tile (the row
         // is that share's last segment), slot 0 in every later share (the
         // row is that share's first segment)
         const int slot = k == kf ? 1 : 0;
-        return ((k * a.num_kv_heads + kvh) * 2 + slot) * group + qi;
-    };
-    // kMergeShares shares per round, their m, l and acc loads all in flight
-    // together (rows rarely span more); across rounds a running maximum M
-    // rescales what has been summed (the log-sum-exp combine, one round at a
-    // time)
-    float num[NC] = {};
-    float den = 0.0f, M = -INFINITY;
-    for (int64_t k0 = kf; k0 <= kl; k0 += kMergeShares) {
-        float m[kMergeShares], l[kMergeShares], x[kMergeShares][NC];
+        const int64_t e = ((k * a.num_kv_heads + kvh) * 2 + slot) * group + qi;
+        const float m = live ? a.part[nslot * D + e] : -INFINITY;
+        const float l = live ? a.part[nslot * (D + 1) + e] : 0.0f;
+        const uint64_t lives = __builtin_amdgcn_ballot_w64(live);
+        float x[kMergeShares][NC];
 #pragma unroll
-        for (int u = 0; u < kMergeShares; ++u) {
-            bool live;
-            const int64_t e = entry(k0 + u, live);
-            m[u] = live ? a.part[nslot * D + e] : -INFINITY;
-            l[u] = live ? a.part[nslot * (D + 1) + e] : 0.0f;
+        for (int v = 0; v < kMergeShares; ++v) {
+            const int64_t ev = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(e >> 32), v) << 32) |
+                                         (uint32_t)__builtin_amdgcn_readlane((int)e, v));
 #pragma unroll
-            for (int c = 0; c < NC; ++c) x[u][c] = live ? a.part[e * D + lane + 64 * c] : 0.0f;
+            for (int cc = 0; cc < NC; ++cc)
+                x[v][cc] = (lives >> v & 1) ? a.part[ev * D + lane + 64 * cc] : 0.0f;
         }
+        float mv[kMergeShares], lvv[kMergeShares];
         float mn = M;
 #pragma unroll
-        for (int u = 0; u < kMergeShares; ++u) mn = fmaxf(mn, m[u]);
+        for (int v = 0; v < kMergeShares; ++v) {
+            mv[v] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), v));
+            lvv[v] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), v));
+            mn = fmaxf(mn, mv[v]);
+        }
         const float al = mn == M ? 1.0f : __builtin_amdgcn_exp2f(M - mn);  // 0 on the first round
         den *= al;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) num[c] *= al;
+        for (int cc = 0; cc < NC; ++cc) num[cc] *= al;
 #pragma unroll
-        for (int u = 0; u < kMergeShares; ++u) {
-            const float w = m[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[u] - mn);
-            den += w * l[u];
+        for (int v = 0; v < kMergeShares; ++v) {
+            const float w = mv[v] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv[v] - mn);
+            den += w * lvv[v];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) num[c] += w * x[u][c];
+            for (int cc = 0; cc < NC; ++cc) num[cc] += w * x[v][cc];
         }
         M = mn;
     }

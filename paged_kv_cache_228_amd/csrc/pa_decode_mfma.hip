@@ -796,8 +796,8 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
             if (lane == 0) a.rows[S] = costs_w[S] = carry;
         }
         const int64_t T = uniform(carry);
-        r.p0 = share * T / K;
-        r.p1 = (share + 1) * T / K;
+        r.p0 = div_floor(share * T, K);
+        r.p1 = div_floor((share + 1) * T, K);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint64_t hit = __builtin_amdgcn_ballot_w64(nb[u] > 0 && ex[u] <= r.p0 && r.p0 < ex[u] + nb[u]);

@@ -19,8 +19,9 @@ constexpr int kPrepThreads = 1024; // the prefix-sum kernel's one workgroup
 
 // Work decomposition of the decode: for every KV head, the tiles of all
 // sequences in order (sequence-major, block-minor; T = sum of blocks per
-// sequence) are cut into `shares` contiguous ranges of equal length
-// (share k: [k T / shares, (k + 1) T / shares)); one wave per (share, KV head).
+// sequence) are cut into `shares` contiguous ranges of equal cost, where a
+// sequence costs its tiles plus row_cost (pa_split.h; with row cost 0 share
+// k is [k T / shares, (k + 1) T / shares)); one wave per (share, KV head).
 // A (sequence, KV head) row lying inside one share is finished by that wave;
 // a row cut by share boundaries leaves one partial per share, merged by a
 // second kernel. The tile prefix sums of the rows come from the context

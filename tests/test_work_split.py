@@ -5,7 +5,8 @@ lie on a cost line: a row of nb > 0 tiles costs R = nb + c (c, the row cost,
 is 3 tiles for fp16 and 8 for INT8 and FP8), spread over its tiles, so tile j
 of the row covers [C + j R / nb, C + (j + 1) R / nb) with C the cost of the
 rows before it (integer division); up to 256 sequences, rows that all have
-the same length take c = 0. The total cost Q is cut at
+the same length take c = 0, and so does every batch of at most 64 possible
+blocks per KV head (the library passes it c = 0). The total cost Q is cut at
 b_k = k Q / K into K shares; a tile belongs to the share holding the last
 unit of its interval. pa_split.h and the prep, decode and merge kernels use
 the integer formulas restated below. A wave finds its share's ends either by
@@ -218,3 +219,36 @@ def test_row_cost_moves_tiles_off_shares_that_start_many_rows():
     lengths = [p1 - p0 for p0, p1 in sh]
     assert lengths[0] < lengths[-1]
     assert walk(ctxs, 8, 96, 0) == [(k * 192 // 8, (k + 1) * 192 // 8) for k in range(8)]
+
+
+def _div_floor_model(x, y, rel_err):
+    """The split's integer division as the kernels do it: a reciprocal of y with
+    relative error rel_err (the hardware's is 2^-23 or better), two Newton
+    steps, the double-precision estimate of x / y truncated, then at most one
+    exact integer correction either way; None if more would be needed."""
+    yd = float(y)
+    r = (1.0 / yd) * (1.0 + rel_err)
+    for _ in range(2):
+        r = r + r * (1.0 - yd * r)
+    q = int(float(x) * r)
+    if q * y > x:
+        q -= 1
+    elif (q + 1) * y <= x:
+        q += 1
+    return q if q * y <= x < (q + 1) * y else None
+
+
+def test_div_floor_estimate_is_within_one():
+    # every quotient of the split is below 2^31; numerators reach k * Q with
+    # k < 2^16 shares per head; the reciprocal taken 2^10 times worse than the
+    # hardware's promise still leaves the estimate within one
+    rng = random.Random(5)
+    cases = [(0, 1), (1, 1), (2**31 - 1, 1), (2**62, 2**31 + 5), (2**47 - 1, 2**16 - 1)]
+    for _ in range(20000):
+        y = rng.choice([rng.randint(1, 64), rng.randint(1, 2**16), rng.randint(1, 2**31 - 1)])
+        q = rng.randint(0, 2**31 - 1)
+        x = q * y + rng.choice([0, 1, y - 1, rng.randint(0, y - 1)])
+        cases.append((x, y))
+    for x, y in cases:
+        for e in (0.0, 2.0**-13, -(2.0**-13)):
+            assert _div_floor_model(x, y, e) == x // y, (x, y, e)
