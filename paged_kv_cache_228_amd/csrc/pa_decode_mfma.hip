@@ -756,7 +756,8 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int s = 64 * u + lane;
-        nb[u] = s < S ? clamp_blocks(a.ctx[s], a.max_blocks) : 0;
+        const int x = a.ctx[s < S ? s : S - 1];  // unconditional: the four loads in flight together
+        nb[u] = s < S ? clamp_blocks(x, a.max_blocks) : 0;
     }
     // exclusive tile prefix sums (a 64-lane scan per 64 rows)
     int carry = 0;
@@ -873,6 +874,9 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     // kernels ran 30 µs slower on the mixed batch (and 4 to 11 µs slower on
     // batches with no sharing at all), far more than the caching gains.
     constexpr bool kShareAware = F == kKvF16;
+    // the group argument (after the struct) loads with the struct's fields,
+    // not on its own later in the prologue
+    asm volatile("" ::"s"(group));
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;

@@ -17,16 +17,14 @@ namespace pa {
 
 // floor(x / y) for 0 <= x < 2^63 and 0 < y, when the quotient is below 2^31
 // (every quotient of the split is: a share index, a tile index or a cost
-// below 2^31). Operands below 2^32 (the usual case) take the 32-bit unsigned
-// division; larger ones a double-precision estimate, within one of the
-// quotient, corrected exactly in integers: much shorter code than a 64-bit
-// division. The estimate multiplies by the hardware reciprocal of y refined
-// by two Newton steps (each squares the relative error: from the
+// below 2^31): a double-precision estimate, within one of the quotient, then
+// corrected exactly in integers, branch-free and much shorter code than a
+// 64-bit division. The estimate multiplies by the hardware reciprocal of y
+// refined by two Newton steps (each squares the relative error: from the
 // reciprocal's 2^-23 or better to the rounding of double arithmetic), so x/y
 // is off by far less than one for quotients below 2^31.
 __device__ __forceinline__ int64_t div_floor(int64_t x, int64_t y)
 {
-    if (((uint64_t)x | (uint64_t)y) >> 32 == 0) return (int64_t)((uint32_t)x / (uint32_t)y);
     const double yd = (double)y;
     double r = __builtin_amdgcn_rcp(yd);
     r = __builtin_fma(__builtin_fma(-yd, r, 1.0), r, r);

@@ -1,0 +1,45 @@
+"""The decode and merge kernels keep every value in registers: the compiler's
+resource report for the library's own build flags shows no scratch memory
+and no spilled VGPRs in any kernel (a spill adds scratch traffic to every
+tile of the hot loop). Host-only: compiles the sources for gfx950 with
+hipcc and reads the report; skipped where hipcc is absent."""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from paged_kv_cache_228_amd import build as B
+
+SOURCES = ("pa_decode_mfma.hip", "pa_decode.hip")
+
+
+def _report(src):
+    out = os.path.join("/tmp", f"resources_{os.getpid()}_{src}.o")
+    r = subprocess.run([B.HIPCC, *B.FLAGS, "-x", "hip", "-Rpass-analysis=kernel-resource-usage", "-c",
+                        os.path.join(B.CSRC, src), "-o", out], capture_output=True, text=True)
+    if os.path.exists(out):
+        os.remove(out)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = {}
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill): (\d+)", line)
+        if m and cur:
+            kernels[cur][m.group(1)] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_scratch_no_spills(src):
+    kernels = _report(src)
+    assert kernels, "no kernel in the resource report"
+    for name, r in kernels.items():
+        assert r.get("ScratchSize [bytes/lane]") == 0, (name, r)
+        assert r.get("VGPRs Spill") == 0, (name, r)
