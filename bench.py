@@ -53,11 +53,25 @@ METRIC = "decode attn tokens/sec + achieved HBM GB/s (% of peak), fp16 & INT8 KV
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 
 
+def code_digest(path: str) -> str:
+    """SHA-256 of a C/C++/HIP source with its comments and whitespace removed:
+    the code the counters were taken with, unchanged by edits to comments."""
+    import hashlib
+    import re
+
+    with open(path) as f:
+        text = f.read()
+    # string literals are kept whole (inline asm templates live in them);
+    # comments and runs of whitespace become one space
+    token = re.compile(r'("(?:\\.|[^"\\])*")|((?://[^\n]*|/\*.*?\*/|\s+)+)|([^"/\s]+|/)', re.S)
+    code = "".join(m.group(1) or (" " if m.group(2) else m.group(3)) for m in token.finditer(text))
+    return hashlib.sha256(code.strip().encode()).hexdigest()
+
+
 def measured_traffic(call: str, workload: str):
     """HBM bytes per launch of `call` from the committed counter profile, or None
-    when there is none for this workload or the kernel sources changed since."""
-    import hashlib
-
+    when there is none for this workload or the kernel sources changed since
+    (comments aside)."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -66,9 +80,8 @@ def measured_traffic(call: str, workload: str):
     if rec is None:
         return None
     for src, digest in rec["sources"].items():
-        with open(os.path.join(ROOT, src), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != digest:
-                return None
+        if code_digest(os.path.join(ROOT, src)) != digest:
+            return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 

@@ -9,10 +9,11 @@
 // (glossary monograph, section 2.1).
 //
 // 1. the work split: the context lengths become tile prefix sums
-//    rows[s] = sum_{s' < s} ceil(ctx_s' / 16) (total T = rows[S]). Up to
-//    kScanSeqs sequences every decode wave scans them itself; beyond that
-//    the prep kernel below does it once, before the waves, and also stores
-//    for every share k of [0, T) the row holding its first tile k T / shares.
+//    rows[s] = sum_{s' < s} ceil(ctx_s' / 16) (total T = rows[S]) and cost
+//    prefix sums (each row with tiles also costs the row cost; pa_split.h).
+//    Up to kScanSeqs sequences every decode wave scans them itself; beyond
+//    that the prep kernel below does it once, before the waves, and also
+//    stores for every share k the row whose cost range holds b_k = k Q / K.
 // 2. the decode waves (pa_decode_mfma.hip) stream their shares; rows inside
 //    one share are finished there, cut rows leave one partial per share.
 // 3. merge: one wave per (sequence, query head) of a cut row combines its

@@ -225,16 +225,22 @@ def test_bench_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypa
 
     (tmp_path / "profiles").mkdir()
     src = tmp_path / "k.hip"
-    src.write_text("kernel v1\n")
+    src.write_text('int v = 1; // the kernel\nasm("s_nop 0  // x");\n')
+    code = 'int v = 1; asm("s_nop 0  // x");'
     rec = {"calls": {"pa_paged_decode_f16": {
         "fetch_bytes": 1000, "write_bytes": 24,
-        "sources": {"k.hip": hashlib.sha256(b"kernel v1\n").hexdigest()}}}}
+        "sources": {"k.hip": hashlib.sha256(code.encode()).hexdigest()}}}}
     (tmp_path / "profiles" / "hbm_traffic_wl.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("pa_paged_decode_f16", "wl") == 1024
     assert bench.measured_traffic("pa_paged_decode_int8", "wl") is None
     assert bench.measured_traffic("pa_paged_decode_f16", "other") is None
-    src.write_text("kernel v2\n")
+    # comments and layout may change; code, string literals included, may not
+    src.write_text('/* v1 */ int v = 1;\n\n  asm("s_nop 0  // x"); // done\n')
+    assert bench.measured_traffic("pa_paged_decode_f16", "wl") == 1024
+    src.write_text('int v = 1; asm("s_nop 0 // x");\n')
+    assert bench.measured_traffic("pa_paged_decode_f16", "wl") is None
+    src.write_text('int v = 2; // the kernel\nasm("s_nop 0  // x");\n')
     assert bench.measured_traffic("pa_paged_decode_f16", "wl") is None
 
 
