@@ -31,11 +31,17 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Device code only: the first kernel arguments of a kernel that takes them as
+# plain scalars or pointers arrive in registers when its waves start (the
+# decode and merge kernels put what their first loads need there), instead
+# of after a load of the argument block; the code object keeps a short entry
+# that loads them for firmware without this.
+HIP_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=8"]
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    lang = ["-x", "hip", *HIP_FLAGS] if src.endswith(".hip") else []
     cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

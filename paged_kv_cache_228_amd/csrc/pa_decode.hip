@@ -93,8 +93,16 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(DecodeArgs a)
 constexpr int kMergeShares = 8;
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a, int group)
+__global__ __launch_bounds__(64) void decode_merge_kernel(int32_t* rows, int num_seqs, int shares,
+                                                          int num_kv_heads, int group, DecodeArgs args)
 {
+    // the leading arguments (the same values as args' fields) are preloaded
+    // into registers, so the first loads wait for no argument load
+    DecodeArgs a = args;
+    a.rows = rows;
+    a.num_seqs = num_seqs;
+    a.shares = shares;
+    a.num_kv_heads = num_kv_heads;
     const int hq = blockIdx.x, s = blockIdx.y;
     const int lane = threadIdx.x;
     const int32_t* costs = a.rows + ws_costs(a.num_seqs);
@@ -231,8 +239,12 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, int group, int fmt, 
     e = launch_decode_waves(a, head_dim, group, fmt, st);
     if (e != hipSuccess) return e;
     const dim3 grid(a.num_q_heads, a.num_seqs);
-    if (head_dim == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, st, a, group);
-    else if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(64), 0, st, a, group);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, st, a.rows, a.num_seqs, a.shares,
+                           a.num_kv_heads, group, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(64), 0, st, a.rows, a.num_seqs, a.shares,
+                           a.num_kv_heads, group, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -753,12 +753,14 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
         return r;
     }
     int nb[4], ex[4], exc[4];
+    // the four loads unconditional (a lane past the batch reads the last
+    // sequence) and in flight together: one memory round trip
+    int x[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int s = 64 * u + lane;
-        const int x = a.ctx[s < S ? s : S - 1];  // unconditional: the four loads in flight together
-        nb[u] = s < S ? clamp_blocks(x, a.max_blocks) : 0;
-    }
+    for (int u = 0; u < 4; ++u) x[u] = a.ctx[min(64 * u + lane, S - 1)];
+    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) nb[u] = 64 * u + lane < S ? clamp_blocks(x[u], a.max_blocks) : 0;
     // exclusive tile prefix sums (a 64-lane scan per 64 rows)
     int carry = 0;
     uint64_t live[4];
@@ -865,8 +867,20 @@ __device__ __forceinline__ ShareLoc locate_share(const DecodeArgs& a, int share,
 // the pool) are read at about the same time, each head by the same compute
 // die throughout.
 template <int D, int F, int SLOT, int MINW>
-__global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int group)
+__global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ctx, int32_t* rows, int num_seqs,
+                                                               int max_blocks, int num_kv_heads, int shares,
+                                                               int row_cost, int group, DecodeArgs args)
 {
+    // the leading arguments (the same values as args' fields) are preloaded
+    // into registers, so the work split's loads wait for no argument load
+    DecodeArgs a = args;
+    a.ctx = ctx;
+    a.rows = rows;
+    a.num_seqs = num_seqs;
+    a.max_blocks = max_blocks;
+    a.num_kv_heads = num_kv_heads;
+    a.shares = shares;
+    a.row_cost = row_cost;
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
     // Blocks shared with a neighbouring row are read with the default cache
@@ -874,9 +888,6 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(DecodeArgs a, int
     // kernels ran 30 µs slower on the mixed batch (and 4 to 11 µs slower on
     // batches with no sharing at all), far more than the caching gains.
     constexpr bool kShareAware = F == kKvF16;
-    // the group argument (after the struct) loads with the struct's fields,
-    // not on its own later in the prologue
-    asm volatile("" ::"s"(group));
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;
@@ -1086,8 +1097,8 @@ template <int D, int F, int SLOT, int MINW>
 hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
 {
     const int64_t waves = (int64_t)a.shares * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, F, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a,
-                       group);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, F, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a.ctx,
+                       a.rows, a.num_seqs, a.max_blocks, a.num_kv_heads, a.shares, a.row_cost, group, a);
     return hipGetLastError();
 }
 

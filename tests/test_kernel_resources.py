@@ -18,7 +18,7 @@ SOURCES = ("pa_decode_mfma.hip", "pa_decode.hip")
 
 def _report(src):
     out = os.path.join("/tmp", f"resources_{os.getpid()}_{src}.o")
-    r = subprocess.run([B.HIPCC, *B.FLAGS, "-x", "hip", "-Rpass-analysis=kernel-resource-usage", "-c",
+    r = subprocess.run([B.HIPCC, *B.FLAGS, "-x", "hip", *B.HIP_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
                         os.path.join(B.CSRC, src), "-o", out], capture_output=True, text=True)
     if os.path.exists(out):
         os.remove(out)
