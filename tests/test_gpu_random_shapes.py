@@ -2,9 +2,10 @@
 in-wave scan's limit (256 sequences) and the prep kernel's path, 1 to 8 KV
 heads, group sizes 1 to 8, head dims 64 and 128, ragged and empty contexts,
 prefix-sharing groups, and explicit share lengths as well as the automatic
-one. Every case runs the fp16 and the INT8 decode with their dead slots
-poisoned (NaN fp16, +-127 INT8 codes) and compares every output element with
-the oracle at the parity bars (2e-3 fp16, 1e-3 INT8)."""
+one. Every case runs the fp16, INT8 and FP8 decodes with their dead slots
+poisoned (NaN fp16, +-127 INT8 codes, random FP8 bytes) and compares every
+output element with the oracle at the parity bars (2e-3 fp16, 1e-3 INT8 and
+FP8)."""
 
 import numpy as np
 import pytest
@@ -13,6 +14,8 @@ import oracle
 from paged_kv_cache_228_amd import workloads as W
 
 from gpu_util import decode_f16, decode_int8, poison_codes, say
+from test_gpu_fp8 import gpu_decode as decode_fp8
+from test_gpu_fp8 import poison as poison_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -56,4 +59,12 @@ def test_random_shape(seed):
     out8 = decode_int8(w, poison_codes(w, kc), poison_codes(w, vc), ks, vs, partition_tokens=pt)
     ref8 = oracle.decode_workload_int8(w, kc, vc, ks, vs)
     assert np.max(np.abs(out8 - ref8)) <= TOL_I8
-    assert not out[w.context_lens <= 0].any() and not out8[w.context_lens <= 0].any()
+    fk, fks = oracle.quantize_kv_fp8(w.k_pool)
+    fv, fvs = oracle.quantize_kv_fp8(w.v_pool)
+    out_f8 = decode_fp8(w, poison_fp8(w, fk, seed), poison_fp8(w, fv, seed + 100), fks, fvs,
+                        partition_tokens=pt)
+    ref_f8 = oracle.paged_decode_fp8(w.q, fk, fv, fks, fvs, w.block_tables, w.context_lens,
+                                     w.softmax_scale)
+    assert np.max(np.abs(out_f8 - ref_f8)) <= TOL_I8
+    empty = w.context_lens <= 0
+    assert not out[empty].any() and not out8[empty].any() and not out_f8[empty].any()
