@@ -107,8 +107,8 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
  * (log-sum-exp combine).
  * partition_tokens: the wanted tokens per share for the longest possible
  * batch (num_seqs x max_blocks_per_seq x 16 tokens), a multiple of 16, or 0
- * to let the library size one wave per SIMD of the current device over the
- * KV heads (fewer for small batches: at least 8 blocks of that longest batch
+ * to let the library size one wave per SIMD of the current device (two at
+ * head_dim 64) over the KV heads (fewer for small batches: at least 8 blocks of that longest batch
  * per share, or, when it has at most 64 blocks, one block per share and at
  * most 8 shares per sequence). A share spans sequence boundaries, so this is not a
  * per-sequence context partition: a value of at least num_seqs x
@@ -117,8 +117,9 @@ int pa_quantize_kv_fp8(const void* k_f16, const void* v_f16, uint8_t* k_fp8, uin
  * contexts), while max_blocks_per_seq x 16 still gives num_seqs shares.
  * kv_format: 0 for pa_paged_decode_f16, 1 for pa_paged_decode_int8, 2
  * for pa_paged_decode_fp8 (other values are rejected). The sizing helpers
- * take num_kv_heads and kv_format because the automatic share count spreads
- * one wave per SIMD over the KV heads, for every format.
+ * take num_kv_heads, head_dim and kv_format because the automatic share
+ * count spreads the waves over the KV heads and the waves per SIMD depend on
+ * the head dimension (and may depend on the format).
  *
  * pa_decode_shares returns the number of shares per KV head, or a negative
  * PA_ERR_* code for arguments the decode calls would reject.

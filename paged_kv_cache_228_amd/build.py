@@ -36,7 +36,7 @@ FLAGS = [
 # decode and merge kernels put what their first loads need there), instead
 # of after a load of the argument block; the code object keeps a short entry
 # that loads them for firmware without this.
-HIP_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=8"]
+HIP_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=8", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str, verbose: bool) -> str:

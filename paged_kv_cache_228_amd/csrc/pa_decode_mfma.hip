@@ -62,17 +62,6 @@ constexpr float kLazy = 8.0f;                 // log2 headroom before the refere
 constexpr float kPScale = 64.0f;              // P enters the matrix core as p * 2^6 (<= 2^14, INT8 <= 2^15)
 constexpr float kPUnscale = 1.0f / 64.0f;
 
-// Blocks per ring slot (even): a slot's tiles are loaded together and
-// computed together; two slots form the ring.
-#ifndef PA_SLOT_F16
-#define PA_SLOT_F16 4
-#endif
-#ifndef PA_SLOT_I8
-#define PA_SLOT_I8 2
-#endif
-#ifndef PA_SLOT_F8
-#define PA_SLOT_F8 2
-#endif
 // Cache-policy bits of the K/V tile loads: non-temporal (2) for tiles read
 // once; the default policy (0) for blocks the neighbouring rows of the batch
 // also reference (a shared prefix), which other waves of the same die read
@@ -81,21 +70,30 @@ constexpr float kPUnscale = 1.0f / 64.0f;
 #define PA_KV_AUX 2
 #endif
 constexpr int kKvAuxShared = 0;
-// Waves per SIMD the register allocation must leave room for. A ring of two
-// 4-tile fp16 slots needs more than half of the register file, so fp16 is
-// bounded for one wave per SIMD with 32 KiB of loads in flight per wave;
-// INT8 and FP8 tiles are half the size and are bounded for two (256
-// registers), which compiled tighter code than the one-wave bound even
-// though the launch now places one wave per SIMD.
-#ifndef PA_MINW_F16
-#define PA_MINW_F16 1
-#endif
-#ifndef PA_MINW_I8
-#define PA_MINW_I8 2
-#endif
-#ifndef PA_MINW_F8
-#define PA_MINW_F8 2
-#endif
+
+// Launch shape per (head_dim, format), chosen by graph-timed sweeps over the
+// mixed prefix-sharing batch, the uniform 32 x 1,024 and 64 x 2,048-token
+// batches, ragged batches of 300 and 1,000 sequences and the Qwen2-shaped
+// layers:
+//   SLOT  blocks per ring slot (even); two slots form the ring, one slot's
+//         loads in flight while the other is computed. Two everywhere:
+//         4-tile fp16 slots (32 KiB in flight per wave) were 0.4 % slower on
+//         the mixed batch and 4 % slower on 32 x 1,024 tokens, and deeper
+//         one-byte slots slower still.
+//   MINW  waves per SIMD the register allocation leaves room for: fp16 at
+//         d = 128 needs more than 256 registers and gets one; the others fit
+//         256 (the d = 64 kernels under 180).
+//   WAVES waves launched per SIMD. One at d = 128: a second wave per SIMD
+//         ended later than the first, and one wave holding twice the tiles
+//         finished sooner. Two at d = 64, whose tiles are half the size: the
+//         one-byte decodes of the mixed batch at d = 64 took 98 instead of
+//         118 us, fp16 160 instead of 166 us.
+template <int D, int F>
+struct Launch {
+    static constexpr int SLOT = 2;
+    static constexpr int MINW = (D == 128 && F == kKvF16) ? 1 : 2;
+    static constexpr int WAVES = D == 64 ? 2 : 1;
+};
 
 // Element i of a 4-dword vector (i a compile-time constant after unrolling).
 // Written as a select chain: subscripting an array of ext-vector values with
@@ -1093,11 +1091,12 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
     }
 }
 
-template <int D, int F, int SLOT, int MINW>
+template <int D, int F>
 hipError_t launch_waves(const DecodeArgs& a, int group, hipStream_t st)
 {
     const int64_t waves = (int64_t)a.shares * a.num_kv_heads;
-    hipLaunchKernelGGL((decode_mfma_kernel<D, F, SLOT, MINW>), dim3((unsigned)waves), dim3(64), 0, st, a.ctx,
+    hipLaunchKernelGGL((decode_mfma_kernel<D, F, Launch<D, F>::SLOT, Launch<D, F>::MINW>), dim3((unsigned)waves),
+                       dim3(64), 0, st, a.ctx,
                        a.rows, a.num_seqs, a.max_blocks, a.num_kv_heads, a.shares, a.row_cost, group, a);
     return hipGetLastError();
 }
@@ -1111,30 +1110,30 @@ int decode_row_cost(int, int fmt)
     // wave clock stamps put it near 3 us per row touched against 0.7 us per
     // INT8 tile, and a sweep of the mixed-length batch was fastest from 8 to
     // 12 for the one-byte caches (each share then also ends nearer the die
-    // mean); fp16 tiles take twice as long to stream and were flat from 0 to 5.
-    return fmt == kKvF16 ? 3 : 8;
+    // mean); fp16 tiles take twice as long to stream, and with two-tile
+    // slots 6 to 10 suited the ragged batches of 300 and 1,000 sequences
+    // best (2 % and 0.6 % faster than 3), the mixed batch alike within 0.3 %.
+    return fmt == kKvF16 ? 6 : 8;
 }
 
-int decode_waves_per_cu(int, int)
+int decode_waves_per_cu(int head_dim, int fmt)
 {
-    // One wave per SIMD (4 per compute unit), for every format: the INT8 and
-    // FP8 kernels are register-bounded for two waves per SIMD, but a second
-    // round of waves per SIMD ends measurably later than the first, and one
-    // wave per SIMD holding twice the tiles finished the mixed batch sooner.
-    return 4;
+    // four SIMDs per compute unit
+    if (head_dim == 64) return 4 * (fmt == kKvF16 ? Launch<64, kKvF16>::WAVES : Launch<64, kKvI8>::WAVES);
+    return 4 * (fmt == kKvF16 ? Launch<128, kKvF16>::WAVES : Launch<128, kKvI8>::WAVES);
 }
 
 hipError_t launch_decode_waves(const DecodeArgs& a, int head_dim, int group, int fmt, hipStream_t st)
 {
     if (head_dim == 128) {
-        if (fmt == kKvI8) return launch_waves<128, kKvI8, PA_SLOT_I8, PA_MINW_I8>(a, group, st);
-        if (fmt == kKvF8) return launch_waves<128, kKvF8, PA_SLOT_F8, PA_MINW_F8>(a, group, st);
-        return launch_waves<128, kKvF16, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+        if (fmt == kKvI8) return launch_waves<128, kKvI8>(a, group, st);
+        if (fmt == kKvF8) return launch_waves<128, kKvF8>(a, group, st);
+        return launch_waves<128, kKvF16>(a, group, st);
     }
     if (head_dim == 64) {
-        if (fmt == kKvI8) return launch_waves<64, kKvI8, PA_SLOT_I8, PA_MINW_I8>(a, group, st);
-        if (fmt == kKvF8) return launch_waves<64, kKvF8, PA_SLOT_F8, PA_MINW_F8>(a, group, st);
-        return launch_waves<64, kKvF16, PA_SLOT_F16, PA_MINW_F16>(a, group, st);
+        if (fmt == kKvI8) return launch_waves<64, kKvI8>(a, group, st);
+        if (fmt == kKvF8) return launch_waves<64, kKvF8>(a, group, st);
+        return launch_waves<64, kKvF16>(a, group, st);
     }
     return hipErrorInvalidValue;
 }

@@ -182,6 +182,9 @@ def test_workspace_and_share_sizing():
         assert pa.pa_decode_shares(64, 8, 128, 1024, kv_format=fmt) == 128
         assert (pa.pa_decode_workspace_bytes(64, 32, 8, 128, 1024, kv_format=fmt)
                 == ints(64, 128, 8) + 128 * 2 * 32 * 130 * 4)
+    # head dim 64: two waves per SIMD, twice the shares
+    for fmt in (pa.KV_F16, pa.KV_INT8, pa.KV_FP8):
+        assert pa.pa_decode_shares(64, 8, 64, 1024, kv_format=fmt) == 256
     # explicit share length: 1 x 1024 blocks x 16 tokens / 256 tokens
     assert pa.pa_decode_shares(1, 1, 64, 1024, 16, 256) == 64
     # never more shares than blocks in the bound
