@@ -1020,24 +1020,33 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
             for (int u = 0; u < SLOT; ++u) e[u] = mbid[j0_ + u < nloc ? j0_ + u : 0];
         };
         // issue the loads of ring slot r (blocks j0_ .. j0_ + SLOT - 1 of the
-        // chunk), each with its cache policy (an instruction field, so one
-        // branch per tile, compiled in only where it pays: kShareAware)
-        auto load_slot = [&](int r, const int (&e)[SLOT], int j0_) {
+        // chunk) with cache policy AUX (an instruction field)
+        auto load_slot = [&](auto aux, int r, const int (&e)[SLOT], int j0_) {
+            constexpr int AUX = decltype(aux)::value;
 #pragma unroll
             for (int u = 0; u < SLOT; ++u) {
                 const int bid = uniform(e[u]);
                 const bool valid = j0_ + u < nloc;
                 mscales<D, F>(a, bid, valid, kvh, ks[r][u], vs[r][u]);
-                if (kShareAware && j0_ + u < shared_len)
-                    mload<D, F, kKvAuxShared>(ring[r][u], a, bid, valid, kvh, lane);
-                else
-                    mload<D, F, PA_KV_AUX>(ring[r][u], a, bid, valid, kvh, lane);
+                mload<D, F, AUX>(ring[r][u], a, bid, valid, kvh, lane);
             }
         };
+        // Slots before `split` (the chunk's shared run, rounded down to whole
+        // slots) are loaded with the default policy, the rest non-temporally.
+        // The policy is fixed per loop (a shared phase, one step that crosses
+        // into the private blocks, a private phase), never chosen by a branch
+        // inside the loop body: such a branch made the compiler wait for every
+        // load in flight, the next slot's included, before computing a slot.
+        const std::integral_constant<int, kKvAuxShared> shp{};
+        const std::integral_constant<int, PA_KV_AUX> prv{};
+        const int split = kShareAware ? min(shared_len, nloc) / SLOT * SLOT : 0;
         int e0[SLOT], e1[SLOT];
         read_ids(e0, 0);
         read_ids(e1, SLOT);
-        load_slot(0, e0, 0);
+        if (kShareAware && split > 0)
+            load_slot(shp, 0, e0, 0);
+        else
+            load_slot(prv, 0, e0, 0);
 
         if (seg_first) {  // a new row: its query operand and a fresh state
             make_q<D, KI8>(qo, qraw);
@@ -1061,21 +1070,33 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
             if (nc0 == 0) fetch_q<D, KI8>(qraw, q_row(ng.s), qh < group, g);
         }
 
-        for (int jj = 0; jj < nloc; jj += 2 * SLOT) {
+        // one step of the ring: slot jj + SLOT's loads (policy pb) go out,
+        // slot jj is computed, slot jj + 2 SLOT's loads (policy pa) go out,
+        // slot jj + SLOT is computed
+        auto step = [&](int jj, auto pb, auto pa) {
             read_ids(e0, jj + 2 * SLOT);
-            load_slot(1, e1, jj + SLOT);
+            load_slot(pb, 1, e1, jj + SLOT);
             __builtin_amdgcn_sched_barrier(0);
             mslot<D, F, SLOT>(st, ring[0], qo, live - jj * kBlockTokens, a.scale_log2, ks[0], vs[0], lane,
                                lo_sel, kl);
             __builtin_amdgcn_sched_barrier(0);
             read_ids(e1, jj + 3 * SLOT);
-            load_slot(0, e0, jj + 2 * SLOT);
+            load_slot(pa, 0, e0, jj + 2 * SLOT);
             __builtin_amdgcn_sched_barrier(0);
             if (jj + SLOT < nloc)  // a slot wholly past the chunk changes nothing
                 mslot<D, F, SLOT>(st, ring[1], qo, live - (jj + SLOT) * kBlockTokens, a.scale_log2, ks[1],
                                    vs[1], lane, lo_sel, kl);
             __builtin_amdgcn_sched_barrier(0);
+        };
+        int jj = 0;
+        if constexpr (kShareAware) {
+            for (; jj < nloc && jj + 2 * SLOT < split; jj += 2 * SLOT) step(jj, shp, shp);
+            if (jj < nloc && jj + SLOT < split) {  // split == jj + 2 SLOT
+                step(jj, shp, prv);
+                jj += 2 * SLOT;
+            }
         }
+        for (; jj < nloc; jj += 2 * SLOT) step(jj, prv, prv);
 
         if (seg_last) {
             const int nb = nblk(cg.s);
