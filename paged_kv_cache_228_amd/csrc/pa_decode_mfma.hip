@@ -882,10 +882,10 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
     // Blocks shared with a neighbouring row are read with the default cache
-    // policy: fp16 only. With the per-tile policy branch the INT8 and FP8
-    // kernels ran 30 µs slower on the mixed batch (and 4 to 11 µs slower on
-    // batches with no sharing at all), far more than the caching gains.
-    constexpr bool kShareAware = F == kKvF16;
+    // policy, except by the FP8 decode at head dim 128, whose registers the
+    // neighbours' table entries and the extra loop phases overflow (it then
+    // spilled and ran 3 to 14 us slower).
+    constexpr bool kShareAware = !(F == kKvF8 && D == 128);
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;

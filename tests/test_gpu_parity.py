@@ -286,13 +286,15 @@ def test_every_context_empty(path, num_seqs):
 
 
 def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic():
-    """The fp16 decode reads blocks that a neighbouring row's table also names
-    with another cache policy. Filling every row's table past its last block
-    with its neighbours' ids (entries the decode never reads as tiles) makes
-    the comparison find shared runs where there were none; the outputs must
-    stay bit-identical, as must a shared prefix turned private."""
+    """The fp16 and INT8 decodes read blocks that a neighbouring row's table
+    also names with another cache policy. Filling every row's table past its
+    last block with its neighbours' ids (entries the decode never reads as
+    tiles) makes the comparison find shared runs where there were none; the
+    outputs must stay bit-identical, as must a shared prefix turned private."""
     w = workload("mixed_prefix")
+    _, kc, vc, ks, vs = oracle_codes("mixed_prefix")
     base = decode_f16(w)
+    base8 = decode_int8(w, kc, vc, ks, vs)
     t = w.block_tables.copy()
     nb = (w.context_lens + 15) // 16
     for s in range(w.num_seqs):
@@ -300,6 +302,25 @@ def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic():
         t[s, nb[s]:] = src[nb[s]:]
     say("shared-block policy: tables filled with the neighbours' ids")
     assert np.array_equal(decode_f16(w, tables=t).view(np.uint32), base.view(np.uint32))
+    assert np.array_equal(decode_int8(w, kc, vc, ks, vs, tables=t).view(np.uint32), base8.view(np.uint32))
+    # the second row of every sharing group reads its prefix from private
+    # copies of the same blocks: no shared run left for it
+    k, v, t2 = w.k_pool.copy(), w.v_pool.copy(), w.block_tables.copy()
+    kc2, vc2, ks2, vs2 = kc.copy(), vc.copy(), ks.copy(), vs.copy()
+    free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
+    used = 0
+    for s in range(1, w.num_seqs, 4):
+        for j in range(min(64, int(nb[s]))):
+            b, f = t2[s, j], free[used]
+            used += 1
+            k[f], v[f] = k[b], v[b]
+            kc2[f], vc2[f], ks2[f], vs2[f] = kc[b], vc[b], ks[b], vs[b]
+            t2[s, j] = f
+    say(f"shared-block policy: {used} prefix blocks made private")
+    assert np.array_equal(decode_f16(w, k_pool=k, v_pool=v, tables=t2).view(np.uint32),
+                          base.view(np.uint32))
+    assert np.array_equal(decode_int8(w, kc2, vc2, ks2, vs2, tables=t2).view(np.uint32),
+                          base8.view(np.uint32))
     # the second row of every sharing group reads its prefix from private
     # copies of the same blocks: no shared run left for it
     k, v, t2 = w.k_pool.copy(), w.v_pool.copy(), w.block_tables.copy()
