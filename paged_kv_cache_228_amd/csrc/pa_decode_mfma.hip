@@ -80,9 +80,11 @@ constexpr int kKvAuxShared = 0;
 //         4-tile fp16 slots (32 KiB in flight per wave) were 0.4 % slower on
 //         the mixed batch and 4 % slower on 32 x 1,024 tokens, and deeper
 //         one-byte slots slower still.
-//   MINW  waves per SIMD the register allocation leaves room for: fp16 at
-//         d = 128 needs more than 256 registers and gets one; the others fit
-//         256 (the d = 64 kernels under 180).
+//   MINW  waves per SIMD the register allocation leaves room for: fp16 and
+//         FP8 at d = 128 need more than 256 registers and get one (FP8 with
+//         256 spilled once it read shared blocks with their own policy); INT8
+//         at d = 128 and every d = 64 kernel fit 256 (the d = 64 ones under
+//         190).
 //   WAVES waves launched per SIMD. One at d = 128: a second wave per SIMD
 //         ended later than the first, and one wave holding twice the tiles
 //         finished sooner. Two at d = 64, whose tiles are half the size: the
@@ -91,7 +93,7 @@ constexpr int kKvAuxShared = 0;
 template <int D, int F>
 struct Launch {
     static constexpr int SLOT = 2;
-    static constexpr int MINW = (D == 128 && F == kKvF16) ? 1 : 2;
+    static constexpr int MINW = (D == 128 && F != kKvI8) ? 1 : 2;
     static constexpr int WAVES = D == 64 ? 2 : 1;
 };
 
@@ -881,11 +883,6 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
     a.row_cost = row_cost;
     static_assert(SLOT >= 2 && SLOT % 2 == 0, "slots hold pairs of tiles");
     constexpr bool KI8 = MCfg<D, F>::I8;  // K codes on the int8 matrix cores
-    // Blocks shared with a neighbouring row are read with the default cache
-    // policy, except by the FP8 decode at head dim 128, whose registers the
-    // neighbours' table entries and the extra loop phases overflow (it then
-    // spilled and ran 3 to 14 us slower).
-    constexpr bool kShareAware = !(F == kKvF8 && D == 128);
     const int kvh = blockIdx.x % a.num_kv_heads;
     const int share = blockIdx.x / a.num_kv_heads;
     const int lane = threadIdx.x;
@@ -961,12 +958,8 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
             const int i = lane + 64 * r;
             tb[r] = i < nloc ? a.tables[at + i] : -1;
         }
-        if constexpr (kShareAware) {
-            tp = lane < nloc && sg.s > 0 ? a.tables[at - a.max_blocks + lane] : -2;
-            tn = lane < nloc && sg.s + 1 < a.num_seqs ? a.tables[at + a.max_blocks + lane] : -2;
-        } else {
-            tp = tn = -2;
-        }
+        tp = lane < nloc && sg.s > 0 ? a.tables[at - a.max_blocks + lane] : -2;
+        tn = lane < nloc && sg.s + 1 < a.num_seqs ? a.tables[at + a.max_blocks + lane] : -2;
     };
     auto q_row = [&](int row) {
         return static_cast<const _Float16*>(a.q) + ((int64_t)row * a.num_q_heads + kvh * group + qh) * D;
@@ -986,12 +979,8 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
         // references (within its first 64) is read with the default cache
         // policy, the rest non-temporally. Only the policy depends on the
         // neighbours, never the order of the arithmetic.
-        int shared_len = 0;
-        if constexpr (kShareAware) {
-            const uint64_t same =
-                __builtin_amdgcn_ballot_w64(lane < nloc && tb[0] >= 0 && (tb[0] == tp || tb[0] == tn));
-            shared_len = ~same == 0 ? 64 : (int)__builtin_ctzll(~same);
-        }
+        const uint64_t same = __builtin_amdgcn_ballot_w64(lane < nloc && tb[0] >= 0 && (tb[0] == tp || tb[0] == tn));
+        const int shared_len = ~same == 0 ? 64 : (int)__builtin_ctzll(~same);
         const int jb = cg.j + cc0;  // first block of the chunk within the row
         const bool seg_first = cc0 == 0;
         const bool seg_last = cc0 + kMaxChunkBlocks >= cg.nseg;
@@ -1039,11 +1028,11 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
         // load in flight, the next slot's included, before computing a slot.
         const std::integral_constant<int, kKvAuxShared> shp{};
         const std::integral_constant<int, PA_KV_AUX> prv{};
-        const int split = kShareAware ? min(shared_len, nloc) / SLOT * SLOT : 0;
+        const int split = min(shared_len, nloc) / SLOT * SLOT;
         int e0[SLOT], e1[SLOT];
         read_ids(e0, 0);
         read_ids(e1, SLOT);
-        if (kShareAware && split > 0)
+        if (split > 0)
             load_slot(shp, 0, e0, 0);
         else
             load_slot(prv, 0, e0, 0);
@@ -1089,12 +1078,10 @@ __global__ __launch_bounds__(64, MINW) void decode_mfma_kernel(const int32_t* ct
             __builtin_amdgcn_sched_barrier(0);
         };
         int jj = 0;
-        if constexpr (kShareAware) {
-            for (; jj < nloc && jj + 2 * SLOT < split; jj += 2 * SLOT) step(jj, shp, shp);
-            if (jj < nloc && jj + SLOT < split) {  // split == jj + 2 SLOT
-                step(jj, shp, prv);
-                jj += 2 * SLOT;
-            }
+        for (; jj < nloc && jj + 2 * SLOT < split; jj += 2 * SLOT) step(jj, shp, shp);
+        if (jj < nloc && jj + SLOT < split) {  // split == jj + 2 SLOT
+            step(jj, shp, prv);
+            jj += 2 * SLOT;
         }
         for (; jj < nloc; jj += 2 * SLOT) step(jj, prv, prv);
 
