@@ -146,17 +146,6 @@ __device__ __forceinline__ float from_lane(float x, int src)
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
-// Byte b of sign-flipped code words u0 and u1 as an exact fp16 pair. Flipping
-// the sign bit of a code c gives the byte c + 128; under the fp16 pattern
-// 0x64xx that byte reads 1024 + c + 128, and subtracting 1152 leaves c.
-__device__ __forceinline__ uint32_t code_pair(uint32_t u0, uint32_t u1, int b)
-{
-    const uint32_t sel = (uint32_t)b | 0x0C00u | ((uint32_t)(4 + b) << 16) | 0x0C000000u;
-    const uint32_t two = __builtin_amdgcn_perm(u1, u0, sel) | 0x64006400u;
-    const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, two) - bias);
-}
-
 // Half h (0/1) of fp16 words w0 and w1 as a pair.
 __device__ __forceinline__ uint32_t half_pair(uint32_t w0, uint32_t w1, int h)
 {
@@ -440,19 +429,6 @@ __device__ __forceinline__ void make_q(QOp<D, I8>& qo, const QRaw<D, I8>& qr)
     }
 }
 
-// Codes b and b + 1 (b = 0 or 2) of the two tokens whose sign-flipped code
-// words are interleaved in `il` (bytes: token 0's code b, token 1's code b,
-// token 0's code b + 1, token 1's) as two exact fp16 pairs, one per code:
-// each byte goes under the fp16 pattern 0x64xx (a byte permute with a word
-// of 0x64 bytes) and 1152 is subtracted (see code_pair).
-__device__ __forceinline__ uint32_t code_pair_il(uint32_t il, int half)
-{
-    const uint32_t sel = half ? 0x04030402u : 0x04010400u;
-    const uint32_t two = __builtin_amdgcn_perm(0x64646464u, il, sel);
-    const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, two) - bias);
-}
-
 // The four V operand words of a pair of INT8 tiles for code byte B of word
 // x0..x3 (tile a's tokens 4g..4g+3) and y0..y3 (tile b's): each word is
 // the fp16 pair of two consecutive tokens' codes. The conversion takes the
@@ -492,18 +468,13 @@ __device__ __forceinline__ u32x4 i8_vwords_at(int b, uint32_t x0, uint32_t x1, u
     }
 }
 
-// The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1.
+// The V operand word of tile t for dim slot nb and tokens 4g+2h, 4g+2h+1
+// (fp16 and FP8; INT8 tiles take i8_vwords).
 template <int D, int F>
 __device__ __forceinline__ uint32_t v_word(const MTile<D, F>& t, int nb, int h)
 {
-    if constexpr (F == kKvI8) {
-        // the two tokens' sign-flipped code words, interleaved for codes
-        // 4w + 2p and 4w + 2p + 1 (w = nb / 4, p = (nb / 2) % 2)
-        const uint32_t u0 = word(t.v[2 * h], nb >> 2) ^ 0x80808080u;
-        const uint32_t u1 = word(t.v[2 * h + 1], nb >> 2) ^ 0x80808080u;
-        const uint32_t il = __builtin_amdgcn_perm(u1, u0, (nb & 2) ? 0x07030602u : 0x05010400u);
-        return code_pair_il(il, nb & 1);
-    } else if constexpr (F == kKvF8) {
+    static_assert(F != kKvI8, "INT8 V words come from i8_vwords");
+    if constexpr (F == kKvF8) {
         return e4m3_pair2(word(t.v[2 * h], nb >> 2), word(t.v[2 * h + 1], nb >> 2), nb & 3);
     } else {
         return half_pair(word(t.v[2 * h], nb >> 1), word(t.v[2 * h + 1], nb >> 1), nb & 1);
