@@ -286,61 +286,60 @@ def test_every_context_empty(path, num_seqs):
     assert out.shape == (num_seqs, 4, 64) and not out.any()
 
 
-def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic():
+def _mixed_d64():
+    """The mixed batch's lengths and prefix sharing at head dim 64 on a
+    smaller pool: 16 sequences of 512 to 4,096 tokens, groups of 4 sharing
+    their first 64 blocks."""
+    crng = np.random.default_rng(np.random.SeedSequence(233, spawn_key=(9,)))
+    ctx = crng.integers(512, 4097, size=16)
+    return W.build("mixed_d64", 233, ctx, 32, 8, 64, num_blocks=8192, share_groups=4, shared_blocks=64)
+
+
+@pytest.mark.parametrize("name", ["mixed_prefix", "mixed_d64"])
+def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic(name):
     """The decodes (fp16, INT8, FP8) read blocks that a neighbouring row's
     table also names with another cache policy. Filling every row's table past its
     last block with its neighbours' ids (entries the decode never reads as
     tiles) makes the comparison find shared runs where there were none; the
     outputs must stay bit-identical, as must a shared prefix turned private."""
-    w = workload("mixed_prefix")
-    _, kc, vc, ks, vs = oracle_codes("mixed_prefix")
+    if name == "mixed_prefix":
+        w = workload(name)
+        _, kc, vc, ks, vs = oracle_codes(name)
+    else:
+        w = _mixed_d64()
+        kc, ks = oracle.quantize_kv_int8(w.k_pool)
+        vc, vs = oracle.quantize_kv_int8(w.v_pool)
     fk, fks = oracle.quantize_kv_fp8(w.k_pool)
     fv, fvs = oracle.quantize_kv_fp8(w.v_pool)
-    base = decode_f16(w)
-    base8 = decode_int8(w, kc, vc, ks, vs)
-    basef8 = decode_fp8(w, fk, fv, fks, fvs)
+
+    def all_three(k, v, kc_, vc_, ks_, vs_, fk_, fv_, fks_, fvs_, tables):
+        return (decode_f16(w, k_pool=k, v_pool=v, tables=tables),
+                decode_int8(w, kc_, vc_, ks_, vs_, tables=tables),
+                decode_fp8(w, fk_, fv_, fks_, fvs_, tables=tables))
+
+    def same(outs, base):
+        return all(np.array_equal(o.view(np.uint32), b.view(np.uint32)) for o, b in zip(outs, base))
+
+    base = all_three(w.k_pool, w.v_pool, kc, vc, ks, vs, fk, fv, fks, fvs, w.block_tables)
     t = w.block_tables.copy()
     nb = (w.context_lens + 15) // 16
     for s in range(w.num_seqs):
         src = t[s + 1] if s + 1 < w.num_seqs else t[s - 1]
         t[s, nb[s]:] = src[nb[s]:]
-    say("shared-block policy: tables filled with the neighbours' ids")
-    assert np.array_equal(decode_f16(w, tables=t).view(np.uint32), base.view(np.uint32))
-    assert np.array_equal(decode_int8(w, kc, vc, ks, vs, tables=t).view(np.uint32), base8.view(np.uint32))
-    assert np.array_equal(decode_fp8(w, fk, fv, fks, fvs, tables=t).view(np.uint32), basef8.view(np.uint32))
+    say(f"shared-block policy ({name}): tables filled with the neighbours' ids")
+    assert same(all_three(w.k_pool, w.v_pool, kc, vc, ks, vs, fk, fv, fks, fvs, t), base)
     # the second row of every sharing group reads its prefix from private
     # copies of the same blocks: no shared run left for it
-    k, v, t2 = w.k_pool.copy(), w.v_pool.copy(), w.block_tables.copy()
-    kc2, vc2, ks2, vs2 = kc.copy(), vc.copy(), ks.copy(), vs.copy()
-    fk2, fv2, fks2, fvs2 = fk.copy(), fv.copy(), fks.copy(), fvs.copy()
+    pools = [a.copy() for a in (w.k_pool, w.v_pool, kc, vc, ks, vs, fk, fv, fks, fvs)]
+    t2 = w.block_tables.copy()
     free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
     used = 0
     for s in range(1, w.num_seqs, 4):
         for j in range(min(64, int(nb[s]))):
             b, f = t2[s, j], free[used]
             used += 1
-            k[f], v[f] = k[b], v[b]
-            kc2[f], vc2[f], ks2[f], vs2[f] = kc[b], vc[b], ks[b], vs[b]
-            fk2[f], fv2[f], fks2[f], fvs2[f] = fk[b], fv[b], fks[b], fvs[b]
+            for a in pools:
+                a[f] = a[b]
             t2[s, j] = f
-    say(f"shared-block policy: {used} prefix blocks made private")
-    assert np.array_equal(decode_f16(w, k_pool=k, v_pool=v, tables=t2).view(np.uint32),
-                          base.view(np.uint32))
-    assert np.array_equal(decode_int8(w, kc2, vc2, ks2, vs2, tables=t2).view(np.uint32),
-                          base8.view(np.uint32))
-    assert np.array_equal(decode_fp8(w, fk2, fv2, fks2, fvs2, tables=t2).view(np.uint32),
-                          basef8.view(np.uint32))
-    # the second row of every sharing group reads its prefix from private
-    # copies of the same blocks: no shared run left for it
-    k, v, t2 = w.k_pool.copy(), w.v_pool.copy(), w.block_tables.copy()
-    free = np.setdiff1d(np.arange(w.num_blocks), w.block_tables[w.block_tables >= 0])
-    used = 0
-    for s in range(1, w.num_seqs, 4):
-        for j in range(min(64, int(nb[s]))):
-            b, f = t2[s, j], free[used]
-            used += 1
-            k[f], v[f] = k[b], v[b]
-            t2[s, j] = f
-    say(f"shared-block policy: {used} prefix blocks made private")
-    assert np.array_equal(decode_f16(w, k_pool=k, v_pool=v, tables=t2).view(np.uint32),
-                          base.view(np.uint32))
+    say(f"shared-block policy ({name}): {used} prefix blocks made private")
+    assert same(all_three(*pools, t2), base)
