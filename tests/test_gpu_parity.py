@@ -295,6 +295,22 @@ def _mixed_d64():
     return W.build("mixed_d64", 233, ctx, 32, 8, 64, num_blocks=8192, share_groups=4, shared_blocks=64)
 
 
+def test_mixed_d64_matches_oracle():
+    """The mixed batch's shape at head dim 64 (two waves per SIMD, shared
+    prefixes read with their own cache policy): every output element of the
+    fp16, INT8 and FP8 decodes against the oracle at the parity bars."""
+    w = _mixed_d64()
+    say(f"mixed_d64: {w.num_seqs} seqs, {int(w.context_lens.sum())} tokens")
+    assert np.max(np.abs(decode_f16(w) - oracle.decode_workload_f16(w))) <= 2e-3
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs) - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
+    fk, fks = oracle.quantize_kv_fp8(w.k_pool)
+    fv, fvs = oracle.quantize_kv_fp8(w.v_pool)
+    ref = oracle.paged_decode_fp8(w.q, fk, fv, fks, fvs, w.block_tables, w.context_lens, w.softmax_scale)
+    assert np.max(np.abs(decode_fp8(w, fk, fv, fks, fvs) - ref)) <= 1e-3
+
+
 @pytest.mark.parametrize("name", ["mixed_prefix", "mixed_d64"])
 def test_cache_policy_of_shared_blocks_never_changes_the_arithmetic(name):
     """The decodes (fp16, INT8, FP8) read blocks that a neighbouring row's
