@@ -286,6 +286,26 @@ def test_every_context_empty(path, num_seqs):
     assert out.shape == (num_seqs, 4, 64) and not out.any()
 
 
+def test_maximum_sequence_count():
+    """The largest batch the calls accept (65,535 sequences; the merge grid's
+    second dimension): contexts of 0 to 40 tokens, so most rows are short and
+    a tenth are empty, through the prep kernel's path; fp16 and INT8 against
+    the oracle element by element."""
+    rng = np.random.default_rng(65535)
+    ctx = rng.integers(0, 41, size=65535)
+    ctx[rng.random(ctx.size) < 0.1] = 0
+    w = W.build("max_seqs", 65535, ctx.tolist(), 2, 1, 64)
+    say(f"max_seqs: {w.num_seqs} seqs, {int(w.context_lens.sum())} tokens, {w.num_blocks} blocks")
+    out = decode_f16(w)
+    assert np.max(np.abs(out - oracle.decode_workload_f16(w))) <= 2e-3
+    assert not out[w.context_lens <= 0].any()
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    out8 = decode_int8(w, kc, vc, ks, vs)
+    assert np.max(np.abs(out8 - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
+    assert not out8[w.context_lens <= 0].any()
+
+
 def _mixed_d64():
     """The mixed batch's lengths and prefix sharing at head dim 64 on a
     smaller pool: 16 sequences of 512 to 4,096 tokens, groups of 4 sharing
