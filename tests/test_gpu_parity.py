@@ -306,6 +306,21 @@ def test_maximum_sequence_count():
     assert not out8[w.context_lens <= 0].any()
 
 
+def test_very_long_context():
+    """One context of 1,048,576 tokens (65,536 blocks, cut into about 2,000
+    shares whose partials the merge combines in rounds of 8) beside a short,
+    an empty and a mid-length one; fp16 and INT8 against the oracle."""
+    w = W.build("long_ctx", 1048576, [1 << 20, 100, 0, 5000], 4, 1, 64)
+    say(f"long_ctx: {int(w.context_lens.sum())} tokens, {w.num_blocks} blocks")
+    out = decode_f16(w)
+    assert np.max(np.abs(out - oracle.decode_workload_f16(w))) <= 2e-3
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    out8 = decode_int8(w, kc, vc, ks, vs)
+    assert np.max(np.abs(out8 - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
+    assert not out[2].any() and not out8[2].any()
+
+
 def _mixed_d64():
     """The mixed batch's lengths and prefix sharing at head dim 64 on a
     smaller pool: 16 sequences of 512 to 4,096 tokens, groups of 4 sharing
