@@ -321,6 +321,21 @@ def test_very_long_context():
     assert not out[2].any() and not out8[2].any()
 
 
+@pytest.mark.parametrize("hkv,g,d", [(3, 5, 128), (64, 2, 64), (48, 1, 128)])
+def test_kv_head_counts_beyond_eight(hkv, g, d):
+    """KV head counts that are not a power of two or exceed the eight compute
+    dies (the grid's heads-fastest order wraps over the dies unevenly), fp16
+    and INT8 against the oracle."""
+    rng = np.random.default_rng(700 + hkv)
+    ctx = rng.integers(0, 400, size=12)
+    w = W.build(f"heads{hkv}", 700 + hkv, ctx.tolist(), g * hkv, hkv, d)
+    say(f"heads: Hkv={hkv} G={g} d={d}")
+    assert np.max(np.abs(decode_f16(w) - oracle.decode_workload_f16(w))) <= 2e-3
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs) - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
+
+
 def _mixed_d64():
     """The mixed batch's lengths and prefix sharing at head dim 64 on a
     smaller pool: 16 sequences of 512 to 4,096 tokens, groups of 4 sharing
