@@ -42,7 +42,7 @@ def quantize(k_pool, v_pool, block_ids=None):
 
 
 def decode_f16(w: W.Workload, k_pool=None, v_pool=None, tables=None, ctx=None,
-               partition_tokens=0, num_blocks=None):
+               partition_tokens=0, num_blocks=None, scale=None):
     import torch
 
     k = dev(w.k_pool if k_pool is None else k_pool)
@@ -52,14 +52,14 @@ def decode_f16(w: W.Workload, k_pool=None, v_pool=None, tables=None, ctx=None,
     q = dev(w.q)
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
     pa.pa_paged_decode_f16(q, k, v, dev(w.block_tables if tables is None else tables),
-                           dev(w.context_lens if ctx is None else ctx), out, w.softmax_scale,
-                           partition_tokens)
+                           dev(w.context_lens if ctx is None else ctx), out,
+                           w.softmax_scale if scale is None else scale, partition_tokens)
     sync()
     return out.cpu().numpy()
 
 
 def decode_int8(w: W.Workload, kc, vc, ks, vs, tables=None, ctx=None, partition_tokens=0,
-                num_blocks=None):
+                num_blocks=None, scale=None):
     import torch
 
     kc, vc, ks, vs = dev(kc), dev(vc), dev(ks), dev(vs)
@@ -68,8 +68,8 @@ def decode_int8(w: W.Workload, kc, vc, ks, vs, tables=None, ctx=None, partition_
     q = dev(w.q)
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
     pa.pa_paged_decode_int8(q, kc, vc, ks, vs, dev(w.block_tables if tables is None else tables),
-                            dev(w.context_lens if ctx is None else ctx), out, w.softmax_scale,
-                            partition_tokens)
+                            dev(w.context_lens if ctx is None else ctx), out,
+                            w.softmax_scale if scale is None else scale, partition_tokens)
     sync()
     return out.cpu().numpy()
 

@@ -336,6 +336,22 @@ def test_kv_head_counts_beyond_eight(hkv, g, d):
     assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs) - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
 
 
+@pytest.mark.parametrize("scale", [8.0, 1e-3, -0.2])
+def test_softmax_scale_extremes(scale):
+    """A sharp softmax (scale 8: nearly one-hot, the lazy reference max moves
+    often), a flat one (1e-3) and a negative scale, fp16 and INT8 against the
+    oracle."""
+    rng = np.random.default_rng(808)
+    w = W.build("scales", 808, rng.integers(1, 900, size=24).tolist(), 16, 4, 128)
+    say(f"softmax scale {scale}")
+    ref = oracle.paged_decode_f16(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, scale)
+    assert np.max(np.abs(decode_f16(w, scale=scale) - ref)) <= 2e-3
+    kc, ks = oracle.quantize_kv_int8(w.k_pool)
+    vc, vs = oracle.quantize_kv_int8(w.v_pool)
+    ref8 = oracle.paged_decode_int8(w.q, kc, vc, ks, vs, w.block_tables, w.context_lens, scale)
+    assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs, scale=scale) - ref8)) <= 1e-3
+
+
 def _mixed_d64():
     """The mixed batch's lengths and prefix sharing at head dim 64 on a
     smaller pool: 16 sequences of 512 to 4,096 tokens, groups of 4 sharing
