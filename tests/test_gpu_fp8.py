@@ -58,13 +58,14 @@ def gpu_quantize(k_pool, v_pool, block_ids=None):
     return kc.cpu().numpy(), vc.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy()
 
 
-def gpu_decode(w, kc, vc, ks, vs, partition_tokens=0, tables=None):
+def gpu_decode(w, kc, vc, ks, vs, partition_tokens=0, tables=None, scale=None):
     import torch
 
     q = dev(w.q)
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
     pa.pa_paged_decode_fp8(q, dev(kc), dev(vc), dev(ks), dev(vs), dev(w.block_tables if tables is None else tables),
-                           dev(w.context_lens), out, w.softmax_scale, partition_tokens)
+                           dev(w.context_lens), out, w.softmax_scale if scale is None else scale,
+                           partition_tokens)
     sync()
     return out.cpu().numpy()
 

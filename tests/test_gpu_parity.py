@@ -324,8 +324,8 @@ def test_very_long_context():
 @pytest.mark.parametrize("hkv,g,d", [(3, 5, 128), (64, 2, 64), (48, 1, 128)])
 def test_kv_head_counts_beyond_eight(hkv, g, d):
     """KV head counts that are not a power of two or exceed the eight compute
-    dies (the grid's heads-fastest order wraps over the dies unevenly), fp16
-    and INT8 against the oracle."""
+    dies (the grid's heads-fastest order wraps over the dies unevenly), fp16,
+    INT8 and FP8 against the oracle."""
     rng = np.random.default_rng(700 + hkv)
     ctx = rng.integers(0, 400, size=12)
     w = W.build(f"heads{hkv}", 700 + hkv, ctx.tolist(), g * hkv, hkv, d)
@@ -334,13 +334,17 @@ def test_kv_head_counts_beyond_eight(hkv, g, d):
     kc, ks = oracle.quantize_kv_int8(w.k_pool)
     vc, vs = oracle.quantize_kv_int8(w.v_pool)
     assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs) - oracle.decode_workload_int8(w, kc, vc, ks, vs))) <= 1e-3
+    fk, fks = oracle.quantize_kv_fp8(w.k_pool)
+    fv, fvs = oracle.quantize_kv_fp8(w.v_pool)
+    ref = oracle.paged_decode_fp8(w.q, fk, fv, fks, fvs, w.block_tables, w.context_lens, w.softmax_scale)
+    assert np.max(np.abs(decode_fp8(w, fk, fv, fks, fvs) - ref)) <= 1e-3
 
 
 @pytest.mark.parametrize("scale", [8.0, 1e-3, -0.2])
 def test_softmax_scale_extremes(scale):
     """A sharp softmax (scale 8: nearly one-hot, the lazy reference max moves
-    often), a flat one (1e-3) and a negative scale, fp16 and INT8 against the
-    oracle."""
+    often), a flat one (1e-3) and a negative scale, fp16, INT8 and FP8 against
+    the oracle."""
     rng = np.random.default_rng(808)
     w = W.build("scales", 808, rng.integers(1, 900, size=24).tolist(), 16, 4, 128)
     say(f"softmax scale {scale}")
@@ -350,6 +354,10 @@ def test_softmax_scale_extremes(scale):
     vc, vs = oracle.quantize_kv_int8(w.v_pool)
     ref8 = oracle.paged_decode_int8(w.q, kc, vc, ks, vs, w.block_tables, w.context_lens, scale)
     assert np.max(np.abs(decode_int8(w, kc, vc, ks, vs, scale=scale) - ref8)) <= 1e-3
+    fk, fks = oracle.quantize_kv_fp8(w.k_pool)
+    fv, fvs = oracle.quantize_kv_fp8(w.v_pool)
+    reff = oracle.paged_decode_fp8(w.q, fk, fv, fks, fvs, w.block_tables, w.context_lens, scale)
+    assert np.max(np.abs(decode_fp8(w, fk, fv, fks, fvs, scale=scale) - reff)) <= 1e-3
 
 
 def _mixed_d64():
