@@ -1089,10 +1089,11 @@ int decode_row_cost(int, int fmt)
     // wave clock stamps put it near 3 us per row touched against 0.7 us per
     // INT8 tile, and a sweep of the mixed-length batch was fastest from 8 to
     // 12 for the one-byte caches (each share then also ends nearer the die
-    // mean); fp16 tiles take twice as long to stream, and with two-tile
-    // slots 6 to 10 suited the ragged batches of 300 and 1,000 sequences
-    // best (2 % and 0.6 % faster than 3), the mixed batch alike within 0.3 %.
-    return fmt == kKvF16 ? 6 : 8;
+    // mean), 10 being 1.6 % faster than 8 on 300 ragged sequences; fp16
+    // tiles take twice as long to stream, and with two-tile slots 6 to 10
+    // suited the ragged batches of 300 and 1,000 sequences best (2 % and
+    // 0.6 % faster than 3), the mixed batch alike within 0.3 %.
+    return fmt == kKvF16 ? 6 : 10;
 }
 
 int decode_waves_per_cu(int head_dim, int fmt)

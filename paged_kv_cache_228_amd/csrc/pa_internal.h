@@ -69,7 +69,7 @@ inline size_t workspace_bytes(int S, int Hq, int D, int shares)
 __host__ __device__ inline int64_t ws_costs(int S) { return (int64_t)S + 1; }
 __host__ __device__ inline int64_t ws_first_row(int S) { return 2 * ((int64_t)S + 1); }
 // Largest row cost of the work split (decode_row_cost), for the size checks.
-constexpr int kMaxRowCost = 8;
+constexpr int kMaxRowCost = 16;
 
 // pa_paged_decode_int8_noalloc's workspace: a static device array of this
 // many bytes per GPU (PA_NOALLOC_SCRATCH_BYTES in pa.h), whose address on the

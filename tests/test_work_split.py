@@ -178,7 +178,7 @@ def walk(ctxs, K, max_blocks, c):
     return shares
 
 
-@pytest.mark.parametrize("c", [0, 3, 6, 8])
+@pytest.mark.parametrize("c", [0, 3, 6, 8, 10])
 @pytest.mark.parametrize("K", [1, 2, 3, 5, 8, 13, 64, 300])
 def test_random_batches(K, c):
     rng = random.Random(K * 10 + c)
@@ -188,7 +188,7 @@ def test_random_batches(K, c):
         walk(ctxs, K, mb, c)
 
 
-@pytest.mark.parametrize("c", [0, 3, 6, 8])
+@pytest.mark.parametrize("c", [0, 3, 6, 8, 10])
 def test_edge_batches(c):
     walk([0, 0, 0], 4, 8, c)          # nothing to do
     walk([5], 1, 1, c)                # one tile, one share
